@@ -1,0 +1,251 @@
+"""Throughput of the CSA forward on one MI355X (tokens/s), with the sparse-MLA
+kernel's roofline fraction and the CPU oracle as a reported baseline.
+
+    python bench.py [--steps K] [--warmup W] [--workload pack16k] [--seed 0] [--no-cpu-baseline]
+
+A step is one whole forward over the 16384-token THD pack with every input
+already resident in HBM: segment indices, compression of the latent KV and of
+the indexer keys, lightning indexer + top-k, sparse MLA.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "CSA fwd tokens/s (indexer+top-k+sparse MLA), 16k THD pack; % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+MLA_SRC = os.path.join(ROOT, "sparse_attention_thd_amd", "csrc", "csa_mla.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_mla_pack16k.json")
+
+WORKLOAD_TEXT = {
+    "pack16k": "16384-token THD pack (12 segments, lognormal(7,1) lengths, none a multiple of 4), 64 heads x "
+               "d512 shared latent KV (K=V), cmp_ratio 4, window 128, indexer 64x128, top-512, per-head sinks",
+    "single4k": "one 4096-token segment, 64 heads x d512 latent KV, cmp_ratio 4, window 128, indexer 64x128, top-512",
+    "hca32k": "32768-token THD pack (8 segments), cmp_ratio 128 compressor-only, window 128, 64 heads x d512",
+    "cp32k": "context-parallel share: local rows [65536,98304) of a 131072-token pack, prefix KV 98304 rows, "
+             "cmp_ratio 4, indexer 64x128, top-512, 64 heads x d512",
+}
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _dev(a):
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def algorithmic_work(plan, pack):
+    """Attended rows (window + kept compressed rows) and indexer pairs that need scores."""
+    import torch
+    q_pos = plan.q_pos.long()
+    wl, wr = pack.ori_win_left, pack.ori_win_right
+    seg = plan.q_seg.long()
+    cu = plan.L.cu_seqlens_kv.long()
+    t = torch.arange(pack.Tq, device=q_pos.device) + pack.global_start
+    lo = torch.maximum(cu[seg], t - wl)
+    hi = torch.minimum(cu[seg + 1] - 1, t + wr)
+    nwin = (hi - lo + 1).sum().item()
+    nvis = plan.q_cmp_nvis.long()
+    if plan.topk_idx is not None:
+        ncmp = (plan.topk_idx >= 0).sum().item()
+        need = nvis[nvis > pack.topk].sum().item()
+    elif plan.cmp_kv is not None:
+        ncmp = nvis.sum().item()
+        need = 0
+    else:
+        ncmp = need = 0
+    return int(nwin), int(ncmp), int(need)
+
+
+def cpu_baseline(pack, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample: full layout + compression, then
+    indexer + attention for contiguous query chunks until the time budget is spent;
+    the per-query rate is extrapolated to the whole pack."""
+    import oracle
+    from synth import bf16_bits_to_f32
+
+    class Rows:
+        def __init__(self, a):
+            self.a, self.shape = a, a.shape
+
+        def __len__(self):
+            return self.a.shape[0]
+
+        def __getitem__(self, k):
+            v = self.a[k]
+            return bf16_bits_to_f32(v) if v.dtype == np.uint16 else v
+
+    V = {k: (Rows(getattr(pack, k)) if getattr(pack, k) is not None else None)
+         for k in ("q", "ori_kv", "q_I", "k_I", "w")}
+    t0 = time.perf_counter()
+    tabs = oracle.build_indices(pack.cu_seqlens_q, pack.cu_seqlens_kv, pack.global_start, pack.Tq, pack.cmp_ratio,
+                                pack.ori_win_left, pack.ori_win_right)
+    mode = oracle.layer_compress_mode(pack.cmp_ratio, int(tabs["cu_seqlens_cmp"][-1]))
+    cmp_kv = kI = None
+    if mode != oracle.NO_COMPRESS:
+        cmp_kv = oracle.round_to(oracle.compress(V["ori_kv"], pack.cu_seqlens_kv, pack.cmp_ratio), pack.dtype)
+    if mode == oracle.INDEXER:
+        kI = oracle.round_to(oracle.compress(V["k_I"], pack.cu_seqlens_kv, pack.cmp_ratio), pack.dtype)
+    t_fixed = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    done, t_q = 0, 0.0
+    chunk = 64
+    while t_q < budget_s and done < pack.Tq:
+        a = int(rng.integers(0, max(pack.Tq - chunk, 1)))
+        qs = list(range(a, min(a + chunk, pack.Tq)))
+        t1 = time.perf_counter()
+        cmp_idx = None
+        if mode == oracle.INDEXER:
+            idx, _ = oracle.indexer_topk(V["q_I"], V["w"], kI, tabs, pack.topk, queries=qs)
+            cmp_idx = {i: idx[n] for n, i in enumerate(qs)}
+        oracle.sparse_mla_fwd(V["q"], V["ori_kv"], cmp_kv, cmp_idx, tabs, pack.sinks, pack.softmax_scale,
+                              pack.ori_win_left, pack.ori_win_right, pack.cu_seqlens_kv, pack.global_start,
+                              queries=qs, attend_all_visible=(mode == oracle.COMPRESSOR_ONLY))
+        t_q += time.perf_counter() - t1
+        done += len(qs)
+    total = t_fixed + t_q * pack.Tq / done
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    return {"value": pack.Tq / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"layout + compression of the whole pack ({t_fixed:.1f} s), then indexer + attention for "
+                      f"{done} of {pack.Tq} queries in random 64-query chunks ({t_q:.1f} s), extrapolated per query"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pack16k", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design, "
+              f"not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from synth import make_pack
+    from sparse_attention_thd_amd import CsaPlan, ThdLayout
+
+    pack = make_pack(args.workload, args.seed)
+    layout = ThdLayout.from_host(pack.cu_seqlens_q, pack.cu_seqlens_kv, pack.global_start)
+    plan = CsaPlan(layout, H=pack.H, d=pack.d, H_I=pack.H_I, d_I=pack.d_I, cmp_ratio=pack.cmp_ratio,
+                   ori_win_left=pack.ori_win_left, ori_win_right=pack.ori_win_right, topk=pack.topk,
+                   softmax_scale=pack.softmax_scale, dtype=torch.bfloat16)
+    inputs = dict(q=_dev(pack.q), ori_kv=_dev(pack.ori_kv), sinks=_dev(pack.sinks), q_I=_dev(pack.q_I),
+                  k_I=_dev(pack.k_I), w=_dev(pack.w))
+    torch.cuda.synchronize()
+
+    # split the step so the sparse-MLA launch can be bracketed by events on the same stream
+    from sparse_attention_thd_amd import _lib
+    L = plan.L
+
+    def front():
+        _lib.csa_build_indices(L.cu_seqlens_q, L.cu_seqlens_kv, L.B, L.Tq, L.Tkv, L.global_start, plan.r, plan.wl,
+                               plan.wr, plan.q_seg, plan.q_pos, plan.win_idx, plan.cu_seqlens_cmp, plan.cmp_residual,
+                               plan.q_cmp_lo, plan.q_cmp_nvis, plan.cmp_group, plan.Tc_cap)
+        if plan.cmp_kv is not None:
+            _lib.csa_compress(inputs["ori_kv"], L.Tkv, plan.d, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, plan.r,
+                              plan.cmp_kv, plan.Tc_cap)
+        if plan.topk_idx is not None:
+            _lib.csa_compress(inputs["k_I"], L.Tkv, plan.d_I, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, plan.r,
+                              plan.k_I_cmp, plan.Tc_cap)
+
+    def indexer():
+        if plan.topk_idx is not None:
+            _lib.csa_indexer_topk(inputs["q_I"], inputs["w"], plan.k_I_cmp, L.Tq, plan.H_I, plan.d_I, L.cu_seqlens_q,
+                                  L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r,
+                                  L.max_seqlen_kv, plan.topk, plan.topk_idx, None)
+
+    def mla():
+        cmp_idx = plan.topk_idx
+        _lib.csa_sparse_mla_fwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx,
+                                plan.topk if cmp_idx is not None else 0, L.Tq, L.Tkv, plan.H, plan.d, L.cu_seqlens_q,
+                                L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r, plan.wl, plan.wr,
+                                inputs["sinks"], plan.scale, plan.out, None)
+
+    for _ in range(args.warmup):
+        front(); indexer(); mla()
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(E(), E(), E(), E()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1, e2, e3 in ev:
+        e0.record(); front(); e1.record(); indexer(); e2.record(); mla(); e3.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    t_front = np.array([a.elapsed_time(b) for a, b, _, _ in ev])
+    t_idx = np.array([b.elapsed_time(c) for _, b, c, _ in ev])
+    t_mla = np.array([c.elapsed_time(d) for _, _, c, d in ev])
+    t_step = np.array([a.elapsed_time(d) for a, _, _, d in ev])
+    ms_step = float(t_step.mean())
+    tokens_s = pack.Tq / (ms_step / 1e3)
+
+    nwin, ncmp, need = algorithmic_work(plan, pack)
+    mla_flops = 4.0 * pack.H * pack.d * (nwin + ncmp)
+    mla_ms = float(t_mla.mean())
+    mla_tflops = mla_flops / (mla_ms / 1e3) / 1e12
+    idx_flops = 2.0 * pack.H_I * pack.d_I * need
+    idx_ms = float(t_idx.mean())
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tr = json.load(open(TRAFFIC_FILE))
+        if tr.get("kernel_source_sha256_16") == _sha(MLA_SRC) and tr.get("workload") == args.workload:
+            traffic = tr.get("hbm_bytes_per_launch")
+    result = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "seed": args.seed,
+                   "tokens": pack.Tq, "segments": pack.B, "parallelism": "single GPU"},
+        "roofline": {"kernel": "csa_sparse_mla_fwd", "bound": "mfma", "achieved": mla_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": mla_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "algorithmic_flops_per_launch": mla_flops, "attended_rows": nwin + ncmp,
+                     "avg_launch_ms": mla_ms},
+        "phases_ms": {"indices+compress": float(t_front.mean()), "indexer_topk": idx_ms, "sparse_mla": mla_ms,
+                      "step_p10": float(np.percentile(t_step, 10)), "step_p90": float(np.percentile(t_step, 90))},
+        "indexer": {"needed_score_flops": idx_flops,
+                    "mfma_frac": (idx_flops / (idx_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS) if idx_ms > 0 else None},
+        "host_wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(pack, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

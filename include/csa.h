@@ -1,0 +1,201 @@
+/*
+ * csa.h - C ABI of the MI355X (gfx950) library for the forward pass of
+ * DeepSeek-V4 Compressed Sparse Attention (CSA) on a THD-packed token stream.
+ *
+ * Pages cited (by title and section):
+ *   [MI] "PR #2038 完整报告: Enable THD packed-sequence training for
+ *        DeepSeek-V4-Flash, with context parallelism" - 功能与动机, 实现拆解,
+ *        关键源码片段 (thd_utils.py, deepseek_v4.py, compressor.py), 风险与影响.
+ *   [HP] "【RFC】DeepSeek-V4 CSA/HCA 自定义算子接入与对外接口对标 torch_extension" -
+ *        背景, 1. npu_lightning_indexer, 2. npu_sparse_flash_mla,
+ *        缺失入参的用途分析（对照实验）.
+ *   [MS] "MindSpeed-LLM pull 4842" - 主要改动.
+ *   [ML] "feat(deepseek_v4): faithful THD context-parallel path for DS4 CSA
+ *        (bounded activation memory)" - Design, Environment note.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
+ *   row-major.  The library allocates nothing and keeps no state between calls.
+ * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ *   stream) and returns without synchronising.  Outputs are valid once the
+ *   stream reaches that point.
+ * - Host integers size the grids, so no call copies anything device -> host.
+ * - THD layout: `cu_seqlens_kv` [B+1] int32 holds stream-absolute segment
+ *   bounds (the prefix of the stream whose KV is resident; a context-parallel
+ *   rank passes the global segmentation truncated at its KV prefix end).
+ *   `cu_seqlens_q` [B+1] int32 counts this call's local query rows per segment.
+ *   Local query row i is stream row t = global_start + i ([MI] 关键源码片段,
+ *   ThdLayout.from_packed_seq_params); it must lie inside its segment:
+ *   cu_seqlens_q[b] == clamp(cu_seqlens_kv[b] - global_start, 0, Tq) for all b.
+ *   `csa_validate_layout` checks this synchronously; the other calls assume it.
+ * - Compressed rows: segment b owns floor(len_b / r) rows, numbered stream-
+ *   absolutely from cu_seqlens_cmp[b] ([MI] compressor._forward_thd).  Buffers
+ *   of compressed rows are sized Tc_cap >= floor(Tkv / r) >= the true count
+ *   cu_seqlens_cmp[B]; rows at or past the true count are never written.
+ * - dtype: CSA_BF16 (bfloat16 storage, fp32 accumulation) or CSA_F32.
+ *   `sinks`, `lse` and `topk_score` are always float32; indices are int32.
+ * - Return value: CSA_OK or an error code.  All argument checks run on the host
+ *   before any launch, so a failed call enqueues nothing and writes nothing.
+ *   csa_last_error() returns the calling thread's last error message.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* csa_stream_t; /* hipStream_t */
+
+enum {
+  CSA_OK = 0,
+  CSA_EINVAL = 1,        /* a pointer, size or parameter is invalid */
+  CSA_EUNSUPPORTED = 2,  /* a shape combination no kernel is built for */
+  CSA_EHIP = 4           /* the HIP runtime reported an error (message has its text) */
+};
+
+enum { CSA_F32 = 0, CSA_BF16 = 1 };
+
+/* Library version string, e.g. "csa-gfx950 0.1.0". */
+const char* csa_version(void);
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char* csa_last_error(void);
+
+/*
+ * csa_build_indices - segment layout of a THD pack (integer, bit-exact).
+ *
+ * Defined by [MI] 功能与动机 (windows clamp to the query's own segment start,
+ * positions restart per segment, compressor groups respect segment bounds) and
+ * [MI] 关键源码片段 thd_utils.get_window_topk_idxs_thd / compressed_cu_seqlens.
+ *
+ * Outputs, per segment b:
+ *   cu_seqlens_cmp [B+1]  prefix sums of floor(len_b / r)               (required)
+ *   cmp_residual   [B]    len_b mod r, the tail that forms no row ([HP] 背景 1) (required)
+ * per local query row i (t = global_start + i, segment b, p = t - s_b):
+ *   q_seg      [Tq]      b
+ *   q_pos      [Tq]      p (rotary position, restarts per segment)
+ *   win_idx    [Tq, W]   W = ori_win_left + ori_win_right + 1 slots; slot k holds
+ *                        lo + k while lo + k <= hi, else -1, where
+ *                        lo = max(s_b, t - ori_win_left), hi = min(e_b - 1, t + ori_win_right)
+ *   q_cmp_lo   [Tq]      cu_seqlens_cmp[b]
+ *   q_cmp_nvis [Tq]      floor((p + 1) / r): causally complete compressed rows
+ * per compressed row c < cu_seqlens_cmp[B]:
+ *   cmp_group  [Tc_cap]  segment-local group id c - cu_seqlens_cmp[b]
+ * Every per-query / per-row output pointer may be NULL (not written).
+ * Errors: EINVAL for NULL cu_seqlens_*, B < 1, Tq < 0, Tkv < 0, global_start < 0,
+ * global_start + Tq > Tkv, cmp_ratio < 1, a window side < 0, Tc_cap < Tkv / r,
+ * or a NULL required output.
+ */
+int csa_build_indices(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B,
+                      int32_t Tq, int32_t Tkv, int32_t global_start, int32_t cmp_ratio,
+                      int32_t ori_win_left, int32_t ori_win_right,
+                      int32_t* q_seg, int32_t* q_pos, int32_t* win_idx,
+                      int32_t* cu_seqlens_cmp, int32_t* cmp_residual,
+                      int32_t* q_cmp_lo, int32_t* q_cmp_nvis, int32_t* cmp_group,
+                      int32_t Tc_cap, csa_stream_t stream);
+
+/*
+ * csa_compress - segment-local mean pooling of cmp_ratio consecutive rows.
+ *
+ * x [Tkv, d] -> x_cmp [Tc_cap, d]; compressed row c of segment b (group
+ * j = c - cu_seqlens_cmp[b]) is the mean of stream rows s_b + j*r + [0, r)
+ * ([MI] compressor._forward_thd group gather; the learned pooling tail is not
+ * printed there, the mean is this library's operator).  The sum is formed in
+ * float64 in ascending row order and rounded once to the storage dtype (nearest,
+ * ties to even).  Tail rows are never read.  `cu_seqlens_cmp` is the device array
+ * written by csa_build_indices.  Used for the latent KV (d = 512) and the
+ * indexer keys (d = 128).
+ * Errors: EINVAL for NULL pointers, B < 1, Tkv < 0, d < 1, cmp_ratio < 1,
+ * Tc_cap < Tkv / r, unknown dtype; EUNSUPPORTED when d is not a multiple of
+ * 16 bytes' worth of elements (8 for bf16, 4 for f32).
+ */
+int csa_compress(const void* x, int32_t Tkv, int32_t d, int32_t dtype,
+                 const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp, int32_t B,
+                 int32_t cmp_ratio, void* x_cmp, int32_t Tc_cap, csa_stream_t stream);
+
+/*
+ * csa_indexer_topk - lightning indexer scores and per-query top-k within the
+ * query's own segment ([HP] 1. npu_lightning_indexer; [MI] 功能与动机 item 4).
+ *
+ * For local query i in segment b at position p, the candidates are compressed
+ * rows c in [cu_seqlens_cmp[b], cu_seqlens_cmp[b] + floor((p+1)/r)), scored
+ *     score(i, c) = sum_h w[i, h] * max(0, <q_I[i, h, :], k_I_cmp[c, :]>)
+ * with float32 accumulation.  If there are at most `topk` candidates all are
+ * kept; otherwise the `topk` highest scores are kept, exact ties going to the
+ * lower row (-0.0 ranks equal to +0.0).  topk_idx[i, :] lists the kept rows in
+ * ascending order (stream-absolute compressed-row ids, as on [MI] 评论区精华
+ * item 1), then -1.  topk_score (optional, may be NULL) holds each kept row's
+ * score aligned with topk_idx, -inf in empty slots.
+ *   q_I [Tq, H_I, d_I], w [Tq, H_I] (call dtype), k_I_cmp [Tc_cap, d_I] (call dtype,
+ *   from csa_compress), topk_idx [Tq, topk] int32, topk_score [Tq, topk] float32.
+ * `max_seqlen_kv` must bound every segment length; it sizes on-chip score
+ * storage (floor(max_seqlen_kv / r) candidates per query).  Segments longer than
+ * it give unspecified (but in-bounds) results.
+ * Errors: EINVAL for NULL required pointers, B < 1, Tq < 0, H_I < 1, d_I < 1,
+ * topk < 1, cmp_ratio < 1, max_seqlen_kv < 0; EUNSUPPORTED for
+ * floor(max_seqlen_kv / r) > 32768 candidates, topk > 2048, or a shape other
+ * than (H_I, d_I) = (64, 128) bf16 or H_I * d_I <= 8192 with d_I % 8 == 0.
+ */
+int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
+                     int32_t Tq, int32_t H_I, int32_t d_I, int32_t dtype,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                     const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start,
+                     int32_t cmp_ratio, int32_t max_seqlen_kv, int32_t topk,
+                     int32_t* topk_idx, float* topk_score, csa_stream_t stream);
+
+/*
+ * csa_sparse_mla_fwd - sparse MLA forward over one shared latent KV
+ * ([HP] 背景 item 2 and 2. npu_sparse_flash_mla; DS4 geometry d = d_v = 512,
+ * [ML] Environment note).
+ *
+ * For local query i (stream row t, segment b) and head h the keys are
+ *   window rows   ori_kv[lo .. hi], lo = max(s_b, t - ori_win_left),
+ *                 hi = min(e_b - 1, t + ori_win_right)   (band parameters, not an
+ *                 index list: [HP] 对照实验 shows ori_sparse_indices is ignored)
+ *   compressed    cmp_kv[c] for every c >= 0 in cmp_idx[i, 0:topk]  (sparse), or
+ *                 every causally complete row of the segment when cmp_idx is NULL
+ *                 (compressor-only layers, [MS] 主要改动 LayerCompressMode), or
+ *                 none when cmp_kv is NULL (no compression).
+ * Keys are also values (K = V).  One joint softmax spans both branches and the
+ * sink: logits z = softmax_scale * <q[i,h], key>, the sink logit sinks[h] (not
+ * scaled) adds exp(sinks[h]) to the denominator with a zero value.  Online
+ * softmax in float32; MFMA products of bf16 inputs with float32 accumulation.
+ *   q [Tq, H, d], ori_kv [Tkv, d], cmp_kv [Tc_cap, d] (call dtype),
+ *   cmp_idx [Tq, topk] int32, sinks [H] float32 (NULL = no sink),
+ *   out [Tq, H, d] (call dtype), lse [Tq, H] float32 (NULL = not written):
+ *   natural log of the full denominator in the scaled-logit domain.
+ * Errors: EINVAL for NULL q/ori_kv/out/cu_seqlens*, cmp_idx without cmp_kv,
+ * topk < 1 with cmp_idx, B < 1, Tq < 0, a window side < 0, cmp_ratio < 1,
+ * global_start + Tq > Tkv; EUNSUPPORTED for shapes other than (H, d) = (64, 512)
+ * bf16 or H * d <= 8192 with d % 8 == 0, or topk > 2048.
+ */
+int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
+                       int32_t topk, int32_t Tq, int32_t Tkv, int32_t H, int32_t d, int32_t dtype,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                       const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start,
+                       int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
+                       const float* sinks, float softmax_scale, void* out, float* lse,
+                       csa_stream_t stream);
+
+/*
+ * csa_validate_layout - synchronous debug check of a THD layout held in device
+ * memory: cu_seqlens_kv starts at 0, is non-decreasing and ends at Tkv;
+ * cu_seqlens_q equals clamp(cu_seqlens_kv - global_start, 0, Tq); and the longest
+ * segment is at most max_seqlen_kv (pass -1 to skip that check).  Copies the two
+ * arrays to the host (blocks on `stream`).  Returns CSA_OK or CSA_EINVAL with a
+ * message naming the first violated condition.
+ */
+int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B,
+                        int32_t Tq, int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv,
+                        csa_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA_H */

@@ -1,0 +1,147 @@
+"""ctypes binding of libcsa.so: the C ABI declared in include/csa.h, same names.
+
+Argument marshalling only: tensors become device pointers, the stream is torch's
+current stream, and a nonzero status raises ``CsaError`` with the library's
+message.  Every computation happens in the HIP kernels; there is no fallback,
+and importing this module fails loudly when libcsa.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+
+CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP = 0, 1, 2, 4
+CSA_F32, CSA_BF16 = 0, 1
+
+_P = C.c_void_p
+_I = C.c_int32
+
+# name -> argtypes, in the order of include/csa.h
+SIGNATURES = {
+    "csa_version": [],
+    "csa_last_error": [],
+    "csa_build_indices": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P],
+    "csa_compress": [_P, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P],
+    "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
+    "csa_sparse_mla_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P,
+                           C.c_float, _P, _P, _P],
+    "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _P],
+}
+
+
+class CsaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[csa status {code}] {msg}")
+        self.code = code
+
+
+def _load() -> C.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_thd_amd.build`")
+    lib = C.CDLL(LIB_PATH)
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = C.c_char_p if name in ("csa_version", "csa_last_error") else C.c_int
+    return lib
+
+
+LIB = _load()
+
+
+def _check(code: int) -> None:
+    if code != CSA_OK:
+        raise CsaError(code, LIB.csa_last_error().decode())
+
+
+def _ptr(t, name, dtype=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return CSA_BF16
+    if t.dtype == torch.float32:
+        return CSA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def csa_version() -> str:
+    return LIB.csa_version().decode()
+
+
+def csa_last_error() -> str:
+    return LIB.csa_last_error().decode()
+
+
+def csa_build_indices(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, cmp_ratio, ori_win_left,
+                      ori_win_right, q_seg, q_pos, win_idx, cu_seqlens_cmp, cmp_residual, q_cmp_lo, q_cmp_nvis,
+                      cmp_group, Tc_cap, stream=None):
+    i32 = torch.int32
+    _check(LIB.csa_build_indices(
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32), B, Tq, Tkv,
+        global_start, cmp_ratio, ori_win_left, ori_win_right,
+        _ptr(q_seg, "q_seg", i32, True), _ptr(q_pos, "q_pos", i32, True), _ptr(win_idx, "win_idx", i32, True),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), _ptr(cmp_residual, "cmp_residual", i32),
+        _ptr(q_cmp_lo, "q_cmp_lo", i32, True), _ptr(q_cmp_nvis, "q_cmp_nvis", i32, True),
+        _ptr(cmp_group, "cmp_group", i32, True), Tc_cap, _stream(stream)))
+
+
+def csa_compress(x, Tkv, d, cu_seqlens_kv, cu_seqlens_cmp, B, cmp_ratio, x_cmp, Tc_cap, stream=None):
+    i32 = torch.int32
+    _check(LIB.csa_compress(_ptr(x, "x"), Tkv, d, _dtype_code(x), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+                            _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, cmp_ratio,
+                            _ptr(x_cmp, "x_cmp", x.dtype), Tc_cap, _stream(stream)))
+
+
+def csa_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
+                     cmp_ratio, max_seqlen_kv, topk, topk_idx, topk_score=None, stream=None):
+    i32 = torch.int32
+    dt = q_I.dtype
+    _check(LIB.csa_indexer_topk(
+        _ptr(q_I, "q_I"), _ptr(w, "w", dt), _ptr(k_I_cmp, "k_I_cmp", dt), Tq, H_I, d_I, _dtype_code(q_I),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, global_start, cmp_ratio, max_seqlen_kv, topk,
+        _ptr(topk_idx, "topk_idx", i32), _ptr(topk_score, "topk_score", torch.float32, True), _stream(stream)))
+
+
+def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, H, d, cu_seqlens_q, cu_seqlens_kv,
+                       cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, sinks,
+                       softmax_scale, out, lse=None, stream=None):
+    i32 = torch.int32
+    dt = q.dtype
+    _check(LIB.csa_sparse_mla_fwd(
+        _ptr(q, "q"), _ptr(ori_kv, "ori_kv", dt), _ptr(cmp_kv, "cmp_kv", dt, True),
+        _ptr(cmp_idx, "cmp_idx", i32, True), topk, Tq, Tkv, H, d, _dtype_code(q),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True), B, global_start, cmp_ratio, ori_win_left,
+        ori_win_right, _ptr(sinks, "sinks", torch.float32, True), float(softmax_scale), _ptr(out, "out", dt),
+        _ptr(lse, "lse", torch.float32, True), _stream(stream)))
+
+
+def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, stream=None):
+    i32 = torch.int32
+    _check(LIB.csa_validate_layout(_ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+                                   B, Tq, Tkv, global_start, max_seqlen_kv, _stream(stream)))

@@ -1,0 +1,163 @@
+// C ABI of libcsa: host-side argument checks, then kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "../../include/csa.h"
+#include "csa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CSA_OK;
+  return fail(CSA_EHIP, "%s: HIP error %d (%s)", what, static_cast<int>(e), hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t dtype) { return dtype == CSA_F32 || dtype == CSA_BF16; }
+
+constexpr int kMaxTopk = 2048;
+constexpr int kMaxCandidates = 32768;
+
+}  // namespace
+
+extern "C" {
+
+const char* csa_version(void) { return "csa-gfx950 0.1.0"; }
+
+const char* csa_last_error(void) { return g_last_error.c_str(); }
+
+int csa_build_indices(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B, int32_t Tq,
+                      int32_t Tkv, int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left,
+                      int32_t ori_win_right, int32_t* q_seg, int32_t* q_pos, int32_t* win_idx,
+                      int32_t* cu_seqlens_cmp, int32_t* cmp_residual, int32_t* q_cmp_lo, int32_t* q_cmp_nvis,
+                      int32_t* cmp_group, int32_t Tc_cap, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv) return fail(CSA_EINVAL, "csa_build_indices: cu_seqlens_q/kv must not be NULL");
+  if (!cu_seqlens_cmp || !cmp_residual)
+    return fail(CSA_EINVAL, "csa_build_indices: cu_seqlens_cmp and cmp_residual are required outputs");
+  if (B < 1) return fail(CSA_EINVAL, "csa_build_indices: B must be >= 1 (got %d)", B);
+  if (Tq < 0 || Tkv < 0 || global_start < 0)
+    return fail(CSA_EINVAL, "csa_build_indices: Tq, Tkv and global_start must be >= 0");
+  if (static_cast<long long>(global_start) + Tq > Tkv)
+    return fail(CSA_EINVAL, "csa_build_indices: global_start + Tq (%lld) exceeds Tkv (%d)",
+                static_cast<long long>(global_start) + Tq, Tkv);
+  if (cmp_ratio < 1) return fail(CSA_EINVAL, "csa_build_indices: cmp_ratio must be >= 1");
+  if (ori_win_left < 0 || ori_win_right < 0)
+    return fail(CSA_EINVAL, "csa_build_indices: window sides must be >= 0");
+  if (cmp_group && Tc_cap < Tkv / cmp_ratio)
+    return fail(CSA_EINVAL, "csa_build_indices: Tc_cap (%d) < Tkv / cmp_ratio (%d)", Tc_cap, Tkv / cmp_ratio);
+  return hip_status(csa::launch_build_indices(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, cmp_ratio,
+                                              ori_win_left, ori_win_right, q_seg, q_pos, win_idx, cu_seqlens_cmp,
+                                              cmp_residual, q_cmp_lo, q_cmp_nvis, cmp_group, Tc_cap,
+                                              static_cast<hipStream_t>(stream)),
+                    "csa_build_indices");
+}
+
+int csa_compress(const void* x, int32_t Tkv, int32_t d, int32_t dtype, const int32_t* cu_seqlens_kv,
+                 const int32_t* cu_seqlens_cmp, int32_t B, int32_t cmp_ratio, void* x_cmp, int32_t Tc_cap,
+                 csa_stream_t stream) {
+  if (!x || !x_cmp || !cu_seqlens_kv || !cu_seqlens_cmp) return fail(CSA_EINVAL, "csa_compress: NULL pointer");
+  if (B < 1 || Tkv < 0 || d < 1 || cmp_ratio < 1)
+    return fail(CSA_EINVAL, "csa_compress: need B >= 1, Tkv >= 0, d >= 1, cmp_ratio >= 1");
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_compress: unknown dtype %d", dtype);
+  if (Tc_cap < Tkv / cmp_ratio)
+    return fail(CSA_EINVAL, "csa_compress: Tc_cap (%d) < Tkv / cmp_ratio (%d)", Tc_cap, Tkv / cmp_ratio);
+  const int vec = dtype == CSA_BF16 ? 8 : 4;
+  if (d % vec) return fail(CSA_EUNSUPPORTED, "csa_compress: d (%d) must be a multiple of %d", d, vec);
+  return hip_status(csa::launch_compress(x, Tkv, d, dtype, cu_seqlens_kv, cu_seqlens_cmp, B, cmp_ratio, x_cmp,
+                                         Tc_cap, static_cast<hipStream_t>(stream)),
+                    "csa_compress");
+}
+
+int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_t Tq, int32_t H_I, int32_t d_I,
+                     int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                     const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
+                     int32_t max_seqlen_kv, int32_t topk, int32_t* topk_idx, float* topk_score,
+                     csa_stream_t stream) {
+  if (!q_I || !w || !k_I_cmp || !topk_idx || !cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp)
+    return fail(CSA_EINVAL, "csa_indexer_topk: NULL pointer");
+  if (B < 1 || Tq < 0 || H_I < 1 || d_I < 1 || topk < 1 || cmp_ratio < 1 || max_seqlen_kv < 0 || global_start < 0)
+    return fail(CSA_EINVAL, "csa_indexer_topk: invalid size or parameter");
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_indexer_topk: unknown dtype %d", dtype);
+  if (topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_indexer_topk: topk %d > %d", topk, kMaxTopk);
+  const int cap = max_seqlen_kv / cmp_ratio;
+  if (cap > kMaxCandidates)
+    return fail(CSA_EUNSUPPORTED, "csa_indexer_topk: max_seqlen_kv / cmp_ratio = %d candidates > %d", cap,
+                kMaxCandidates);
+  if (!csa::indexer_shape_supported(H_I, d_I, dtype))
+    return fail(CSA_EUNSUPPORTED, "csa_indexer_topk: no kernel for H_I=%d d_I=%d dtype=%d", H_I, d_I, dtype);
+  return hip_status(csa::launch_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, dtype, cu_seqlens_q, cu_seqlens_kv,
+                                             cu_seqlens_cmp, B, global_start, cmp_ratio, cap, topk, topk_idx,
+                                             topk_score, static_cast<hipStream_t>(stream)),
+                    "csa_indexer_topk");
+}
+
+int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
+                       int32_t Tq, int32_t Tkv, int32_t H, int32_t d, int32_t dtype, const int32_t* cu_seqlens_q,
+                       const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp, int32_t B,
+                       int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
+                       const float* sinks, float softmax_scale, void* out, float* lse, csa_stream_t stream) {
+  if (!q || !ori_kv || !out || !cu_seqlens_q || !cu_seqlens_kv)
+    return fail(CSA_EINVAL, "csa_sparse_mla_fwd: NULL pointer");
+  if (cmp_kv && !cu_seqlens_cmp) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: cmp_kv needs cu_seqlens_cmp");
+  if (cmp_idx && !cmp_kv) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: cmp_idx given without cmp_kv");
+  if (cmp_idx && topk < 1) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: topk must be >= 1 with cmp_idx");
+  if (B < 1 || Tq < 0 || Tkv < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0)
+    return fail(CSA_EINVAL, "csa_sparse_mla_fwd: invalid size or parameter");
+  if (ori_win_left < 0 || ori_win_right < 0) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: window sides must be >= 0");
+  if (static_cast<long long>(global_start) + Tq > Tkv)
+    return fail(CSA_EINVAL, "csa_sparse_mla_fwd: global_start + Tq exceeds Tkv");
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: unknown dtype %d", dtype);
+  if (cmp_idx && topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_fwd: topk %d > %d", topk, kMaxTopk);
+  if (!csa::mla_shape_supported(H, d, dtype))
+    return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_fwd: no kernel for H=%d d=%d dtype=%d", H, d, dtype);
+  return hip_status(csa::launch_sparse_mla(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, H, d, dtype, cu_seqlens_q,
+                                           cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left,
+                                           ori_win_right, sinks, softmax_scale, out, lse,
+                                           static_cast<hipStream_t>(stream)),
+                    "csa_sparse_mla_fwd");
+}
+
+int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B, int32_t Tq,
+                        int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv || B < 1 || Tq < 0 || Tkv < 0 || global_start < 0)
+    return fail(CSA_EINVAL, "csa_validate_layout: invalid argument");
+  std::vector<int32_t> cq(B + 1), ck(B + 1);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(cq.data(), cu_seqlens_q, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(ck.data(), cu_seqlens_kv, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "csa_validate_layout");
+  if (ck[0] != 0) return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_kv[0] = %d, expected 0", ck[0]);
+  for (int b = 0; b < B; ++b) {
+    if (ck[b + 1] < ck[b]) return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_kv decreases at %d", b + 1);
+    if (max_seqlen_kv >= 0 && ck[b + 1] - ck[b] > max_seqlen_kv)
+      return fail(CSA_EINVAL, "csa_validate_layout: segment %d has %d rows > max_seqlen_kv %d", b,
+                  ck[b + 1] - ck[b], max_seqlen_kv);
+  }
+  if (ck[B] != Tkv) return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_kv[B] = %d != Tkv = %d", ck[B], Tkv);
+  for (int b = 0; b <= B; ++b) {
+    long long want = static_cast<long long>(ck[b]) - global_start;
+    want = want < 0 ? 0 : (want > Tq ? Tq : want);
+    if (cq[b] != want)
+      return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_q[%d] = %d, expected %lld", b, cq[b], want);
+  }
+  return CSA_OK;
+}
+
+}  // extern "C"

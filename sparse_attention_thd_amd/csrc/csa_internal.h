@@ -1,0 +1,31 @@
+// Internal launcher declarations of libcsa (host side; argument checks happen in csa_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+hipError_t launch_build_indices(const int32_t* cu_q, const int32_t* cu_kv, int B, int Tq, int Tkv,
+                                int global_start, int r, int wl, int wr, int32_t* q_seg, int32_t* q_pos,
+                                int32_t* win_idx, int32_t* cu_cmp, int32_t* residual, int32_t* q_cmp_lo,
+                                int32_t* q_cmp_nvis, int32_t* cmp_group, int Tc_cap, hipStream_t s);
+
+hipError_t launch_compress(const void* x, int Tkv, int d, int dtype, const int32_t* cu_kv,
+                           const int32_t* cu_cmp, int B, int r, void* x_cmp, int Tc_cap, hipStream_t s);
+
+hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp, int Tq, int H_I, int d_I,
+                               int dtype, const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_cmp,
+                               int B, int global_start, int r, int cap, int topk, int32_t* idx, float* score,
+                               hipStream_t s);
+
+hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
+                             int topk, int Tq, int H, int d, int dtype, const int32_t* cu_q,
+                             const int32_t* cu_kv, const int32_t* cu_cmp, int B, int global_start, int r,
+                             int wl, int wr, const float* sinks, float scale, void* out, float* lse,
+                             hipStream_t s);
+
+bool indexer_shape_supported(int H_I, int d_I, int dtype);
+bool mla_shape_supported(int H, int d, int dtype);
+
+}  // namespace csa

@@ -1,0 +1,348 @@
+// Sparse MLA forward: window branch + compressed branch + per-head sink over one
+// shared latent KV (keys are values), fp32 online softmax.
+//
+// MFMA path, (H, d) = (64, 512) bf16: one workgroup of 4 wavefronts per query,
+// wavefront w owning heads [16w, 16w+16).  Keys stream through LDS in tiles of 32
+// rows (window rows first, then the compacted compressed rows).  Per tile:
+//   S^T[32 keys x 16 heads] = K[32 x 512] . Q^T[512 x 16]      (A = K from LDS, B = Q in VGPRs)
+//   online softmax per head in registers (each lane owns one head column)
+//   O^T[512 x 16] += V^T[512 x 32] . P^T[32 x 16]              (A = V^T from LDS, B = P in VGPRs)
+// so the S^T accumulator layout is directly the P^T operand and every lane's
+// O^T accumulators belong to the head whose softmax state it holds.
+//
+// Generic path (H * d <= 8192, either dtype): scalar fp32, one key at a time.
+#include "csa_common.h"
+#include "csa_internal.h"
+
+namespace csa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kMaxTopk = 2048;
+
+struct QueryKeys {
+  int nwin;      // window rows lo .. lo + nwin - 1
+  int lo;
+  int ncmp;      // compressed rows
+  int cmp_base;  // first visible row (attend-all mode)
+};
+
+// Exclusive count of `f` over the block in thread order (block-uniform call).
+__device__ __forceinline__ uint32_t count_excl(bool f, uint32_t* wsum, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const uint32_t in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = __popcll(m);
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    const uint32_t v = wsum[k];
+    off += (k < wave) ? v : 0u;
+    tot += v;
+  }
+  __syncthreads();
+  total = tot;
+  return off + in_wave;
+}
+
+// Resolve the query's window and compressed key ranges; in sparse mode compact
+// the valid entries of cmp_idx[i, :] (in their given order) into crow.
+__device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+                                const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
+                                bool has_cmp, const int32_t* __restrict__ cmp_idx, int topk, int32_t* crow,
+                                uint32_t* wsum) {
+  QueryKeys k;
+  const int b = segment_of(cu_q, B, i);
+  const int t = global_start + i;
+  const int s = cu_kv[b], e = cu_kv[b + 1];
+  k.lo = max(s, t - wl);
+  const int hi = min(e - 1, t + wr);
+  k.nwin = hi - k.lo + 1;
+  k.ncmp = 0;
+  k.cmp_base = cu_cmp[b];
+  if (!has_cmp) return k;
+  if (cmp_idx == nullptr) {
+    const int nv = (t - s + 1) / r;
+    k.ncmp = max(0, min(nv, cu_cmp[b + 1] - k.cmp_base));
+    return k;
+  }
+  const int Tc = cu_cmp[B];
+  const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
+  uint32_t base = 0;
+  for (int j0 = 0; j0 < topk; j0 += kThreads) {
+    const int j = j0 + threadIdx.x;
+    const int c = (j < topk) ? row[j] : -1;
+    const bool ok = c >= 0 && c < Tc;  // entries outside the compressed rows are dropped
+    uint32_t tot;
+    const uint32_t pos = base + count_excl(ok, wsum, tot);
+    if (ok) crow[pos] = c;
+    base += tot;
+  }
+  __syncthreads();
+  k.ncmp = static_cast<int>(base);
+  return k;
+}
+
+// ----------------------------------------------------------------------------- MFMA path
+
+constexpr int kNT = 32;             // keys per tile
+constexpr int kStride = 512 + 8;    // LDS row stride in bf16 elements (1040 bytes)
+
+__global__ __launch_bounds__(kThreads) void mla_fwd_h64_d512_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv,
+    const int32_t* __restrict__ cmp_idx, int topk, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
+    int wr, const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(16))) uint16_t kt[kNT * kStride];
+  __shared__ int32_t crow[kMaxTopk];
+  __shared__ uint32_t wsum[kWaves];
+
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const QueryKeys qk = query_keys(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr, cmp_idx,
+                                  topk, crow, wsum);
+  const int nkeys = qk.nwin + qk.ncmp;
+  const int head = 16 * wave + n;
+
+  // B operand of S^T = K . Q^T: lane (head n, group g) holds q[i, head, 32*ks + 8*g + 0..7]
+  bf16x8 qf[16];
+  {
+    const uint16_t* qrow = q + (static_cast<long long>(i) * 64 + head) * 512 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+  }
+  f32x4 o[32];
+#pragma unroll
+  for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // running max in log2 units; the sink is the initial state (value 0, weight 1 counted once)
+  float m_run = -__builtin_huge_valf();
+  float l_run = 0.f;
+  if (sinks != nullptr) {
+    m_run = sinks[head] * kLog2e;
+    l_run = (g == 0) ? 1.f : 0.f;
+  }
+
+  for (int t0 = 0; t0 < nkeys; t0 += kNT) {
+    // ---- stage 32 key rows (1 KiB each) into LDS; wave w loads rows w, w+4, ...
+#pragma unroll
+    for (int pass = 0; pass < kNT / kWaves; ++pass) {
+      const int rr = pass * kWaves + wave;
+      const int kidx = t0 + rr;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (kidx < nkeys) {
+        const uint16_t* src;
+        if (kidx < qk.nwin) {
+          src = ori_kv + static_cast<long long>(qk.lo + kidx) * 512;
+        } else {
+          const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
+          src = cmp_kv + static_cast<long long>(c) * 512;
+        }
+        v = reinterpret_cast<const uint4*>(src)[lane];
+      }
+      *reinterpret_cast<uint4*>(&kt[rr * kStride + lane * 8]) = v;
+    }
+    __syncthreads();
+
+    // ---- S^T = K . Q^T for keys [16*mb, 16*mb+16)
+    f32x4 s[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(16 * mb + n) * kStride + 32 * ks + 8 * g]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
+      }
+      s[mb] = acc;
+    }
+
+    // ---- online softmax; lane holds keys 16*mb + 4*g + j of head `head`
+    float z[8];
+    float tmax = -__builtin_huge_valf();
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kidx = t0 + 16 * mb + 4 * g + j;
+        const float v = (kidx < nkeys) ? s[mb][j] * scale_log2 : -__builtin_huge_valf();
+        z[4 * mb + j] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = (m_new == -__builtin_huge_valf()) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    bf16x8 pb;
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 ph = static_cast<__bf16>(exp2f(z[j] - m_use));
+      pb[j] = ph;
+      psum += static_cast<float>(ph);
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
+
+    // ---- O^T += V^T . P^T; k-slot 8*g + j <-> key 4*g + j (j < 4) or 16 + 4*g + (j - 4)
+#pragma unroll
+    for (int mb = 0; mb < 32; ++mb) {
+      const int col = 16 * mb + n;
+      uint16_t e[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        e[j] = kt[(4 * g + j) * kStride + col];
+        e[4 + j] = kt[(16 + 4 * g + j) * kStride + col];
+      }
+      bf16x8 a;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a[j] = __builtin_bit_cast(__bf16, e[j]);
+      o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mb], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  float l_tot = l_run;
+  l_tot += __shfl_xor(l_tot, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = 1.f / l_tot;
+  uint16_t* orow = out + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
+#pragma unroll
+  for (int mb = 0; mb < 32; ++mb) {
+    const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0] * inv)) |
+                        (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1] * inv)) << 16);
+    const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2] * inv)) |
+                        (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3] * inv)) << 16);
+    *reinterpret_cast<uint2*>(orow + 16 * mb) = make_uint2(w0, w1);
+  }
+  if (lse != nullptr && g == 0) lse[static_cast<long long>(i) * 64 + head] = m_run * kLn2 + logf(l_tot);
+}
+
+// ----------------------------------------------------------------------------- generic path
+
+__device__ __forceinline__ float ld(const float* p, long long k) { return p[k]; }
+__device__ __forceinline__ float ld(const uint16_t* p, long long k) { return bf16_bits_to_f32(p[k]); }
+__device__ __forceinline__ void st(float* p, long long k, float v) { p[k] = v; }
+__device__ __forceinline__ void st(uint16_t* p, long long k, float v) { p[k] = f32_to_bf16_bits(v); }
+
+constexpr int kGenMaxHD = 8192;
+constexpr int kGenPerThread = kGenMaxHD / kThreads;
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void mla_fwd_generic_kernel(
+    const T* __restrict__ q, const T* __restrict__ ori_kv, const T* __restrict__ cmp_kv,
+    const int32_t* __restrict__ cmp_idx, int topk, int H, int d, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
+    int wr, const float* __restrict__ sinks, float scale, T* __restrict__ out, float* __restrict__ lse) {
+  extern __shared__ float gdyn[];
+  __shared__ int32_t crow[kMaxTopk];
+  __shared__ uint32_t wsum[kWaves];
+  float* qs = gdyn;               // [H*d]
+  float* krow = qs + H * d;       // [d]
+  float* m = krow + d;            // [H]
+  float* l = m + H;               // [H]
+  float* al = l + H;              // [H]
+  float* pv = al + H;             // [H]
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const QueryKeys qk = query_keys(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr, cmp_idx,
+                                  topk, crow, wsum);
+  const int hd = H * d;
+  for (int e = tid; e < hd; e += kThreads) qs[e] = ld(q, static_cast<long long>(i) * hd + e);
+  for (int h = tid; h < H; h += kThreads) {
+    m[h] = sinks ? sinks[h] : -__builtin_huge_valf();
+    l[h] = sinks ? 1.f : 0.f;
+  }
+  float acc[kGenPerThread];
+#pragma unroll
+  for (int u = 0; u < kGenPerThread; ++u) acc[u] = 0.f;
+  __syncthreads();
+  const int nkeys = qk.nwin + qk.ncmp;
+  for (int kidx = 0; kidx < nkeys; ++kidx) {
+    const T* src;
+    if (kidx < qk.nwin) {
+      src = ori_kv + static_cast<long long>(qk.lo + kidx) * d;
+    } else {
+      const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
+      src = cmp_kv + static_cast<long long>(c) * d;
+    }
+    for (int e = tid; e < d; e += kThreads) krow[e] = ld(src, e);
+    __syncthreads();
+    for (int h = tid; h < H; h += kThreads) {
+      float dot = 0.f;
+      for (int e = 0; e < d; ++e) dot += qs[h * d + e] * krow[e];
+      const float z = dot * scale;
+      const float mn = fmaxf(m[h], z);
+      const float a = expf(m[h] - mn);
+      const float p = expf(z - mn);
+      l[h] = l[h] * a + p;
+      m[h] = mn;
+      al[h] = a;
+      pv[h] = p;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kGenPerThread; ++u) {
+      const int e = tid + u * kThreads;
+      if (e < hd) {
+        const int h = e / d;
+        acc[u] = acc[u] * al[h] + pv[h] * krow[e - h * d];
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < kGenPerThread; ++u) {
+    const int e = tid + u * kThreads;
+    if (e < hd) st(out, static_cast<long long>(i) * hd + e, acc[u] / l[e / d]);
+  }
+  if (lse != nullptr)
+    for (int h = tid; h < H; h += kThreads) lse[static_cast<long long>(i) * H + h] = m[h] + logf(l[h]);
+}
+
+}  // namespace
+
+bool mla_shape_supported(int H, int d, int dtype) {
+  if (dtype == 1 && H == 64 && d == 512) return true;
+  return H * d <= kGenMaxHD && d % 8 == 0;
+}
+
+hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
+                             int topk, int Tq, int H, int d, int dtype, const int32_t* cu_q,
+                             const int32_t* cu_kv, const int32_t* cu_cmp, int B, int global_start, int r,
+                             int wl, int wr, const float* sinks, float scale, void* out, float* lse,
+                             hipStream_t s) {
+  if (Tq <= 0) return hipSuccess;
+  if (cmp_idx == nullptr) topk = 0;
+  if (dtype == 1 && H == 64 && d == 512) {
+    hipLaunchKernelGGL(mla_fwd_h64_d512_kernel, dim3(Tq), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, cu_q,
+                       cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale * kLog2e,
+                       static_cast<uint16_t*>(out), lse);
+    return hipGetLastError();
+  }
+  const size_t lds = (static_cast<size_t>(H) * d + d + 4 * static_cast<size_t>(H)) * sizeof(float);
+  if (dtype == 1) {
+    auto k = mla_fwd_generic_kernel<uint16_t>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        static_cast<int>(lds));
+    hipLaunchKernelGGL(k, dim3(Tq), dim3(kThreads), lds, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, H, d,
+                       cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale, static_cast<uint16_t*>(out),
+                       lse);
+  } else {
+    auto k = mla_fwd_generic_kernel<float>;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        static_cast<int>(lds));
+    hipLaunchKernelGGL(k, dim3(Tq), dim3(kThreads), lds, s, static_cast<const float*>(q),
+                       static_cast<const float*>(ori_kv), static_cast<const float*>(cmp_kv), cmp_idx, topk, H, d, cu_q,
+                       cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale, static_cast<float*>(out), lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,113 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments on the host before any HIP call.
+
+Every call here is built to fail validation, so nothing is launched.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+lib_mod = pytest.importorskip("sparse_attention_thd_amd._lib", reason="libcsa.so not built")
+LIB = lib_mod.LIB
+EINVAL, EUNSUP = lib_mod.CSA_EINVAL, lib_mod.CSA_EUNSUPPORTED
+FAKE = 0x1000  # a non-NULL pointer value; validation fails before it could be used
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_steps():
+    names = declared_functions()
+    for n in ("csa_build_indices", "csa_compress", "csa_indexer_topk", "csa_sparse_mla_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    raw = C.CDLL(lib_mod.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(raw, n), n
+        assert n in lib_mod.SIGNATURES, f"binding lacks {n}"
+
+
+def test_version_and_empty_error():
+    assert lib_mod.csa_version().startswith("csa-gfx950")
+
+
+def _bi(**kw):
+    a = dict(cu_q=FAKE, cu_kv=FAKE, B=1, Tq=4, Tkv=4, gs=0, r=4, wl=127, wr=0, q_seg=None, q_pos=None, win=None,
+             cu_cmp=FAKE, res=FAKE, lo=None, nv=None, grp=None, Tc_cap=1, stream=None)
+    a.update(kw)
+    return LIB.csa_build_indices(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cu_q=None), EINVAL), (dict(cu_kv=None), EINVAL), (dict(cu_cmp=None), EINVAL), (dict(res=None), EINVAL),
+    (dict(B=0), EINVAL), (dict(Tq=-1), EINVAL), (dict(Tq=5), EINVAL), (dict(gs=1), EINVAL),
+    (dict(r=0), EINVAL), (dict(wl=-1), EINVAL), (dict(wr=-2), EINVAL), (dict(grp=FAKE, Tc_cap=0, r=2), EINVAL),
+])
+def test_build_indices_rejects(kw, code):
+    assert _bi(**kw) == code
+    assert "csa_build_indices" in lib_mod.csa_last_error()
+
+
+def _cmp(**kw):
+    a = dict(x=FAKE, Tkv=16, d=512, dtype=1, cu_kv=FAKE, cu_cmp=FAKE, B=1, r=4, out=FAKE, Tc_cap=4, stream=None)
+    a.update(kw)
+    return LIB.csa_compress(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), EINVAL), (dict(out=None), EINVAL), (dict(B=0), EINVAL), (dict(d=0), EINVAL),
+    (dict(r=0), EINVAL), (dict(dtype=7), EINVAL), (dict(Tc_cap=3), EINVAL), (dict(d=12), EUNSUP),
+    (dict(d=6, dtype=0), EUNSUP),
+])
+def test_compress_rejects(kw, code):
+    assert _cmp(**kw) == code
+
+
+def _idx(**kw):
+    a = dict(q=FAKE, w=FAKE, k=FAKE, Tq=8, H_I=64, d_I=128, dtype=1, cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE, B=1,
+             gs=0, r=4, maxlen=8, topk=512, idx=FAKE, sc=None, stream=None)
+    a.update(kw)
+    return LIB.csa_indexer_topk(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), EINVAL), (dict(idx=None), EINVAL), (dict(topk=0), EINVAL), (dict(B=0), EINVAL),
+    (dict(maxlen=-1), EINVAL), (dict(dtype=3), EINVAL), (dict(topk=4096), EUNSUP),
+    (dict(maxlen=4 * 40000), EUNSUP), (dict(H_I=128, d_I=128), EUNSUP), (dict(H_I=2, d_I=12, dtype=0), EUNSUP),
+])
+def test_indexer_rejects(kw, code):
+    assert _idx(**kw) == code
+
+
+def _mla(**kw):
+    a = dict(q=FAKE, kv=FAKE, ckv=FAKE, cidx=FAKE, topk=512, Tq=8, Tkv=8, H=64, d=512, dtype=1, cu_q=FAKE,
+             cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, wl=127, wr=0, sinks=None, scale=0.04, out=FAKE, lse=None,
+             stream=None)
+    a.update(kw)
+    return LIB.csa_sparse_mla_fwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), EINVAL), (dict(out=None), EINVAL), (dict(ckv=None), EINVAL), (dict(topk=0), EINVAL),
+    (dict(ckv=FAKE, cu_cmp=None), EINVAL), (dict(B=0), EINVAL), (dict(gs=1), EINVAL), (dict(wl=-1), EINVAL),
+    (dict(dtype=5), EINVAL), (dict(topk=4096), EUNSUP), (dict(H=128), EUNSUP), (dict(H=64, d=256), EUNSUP),
+])
+def test_sparse_mla_rejects(kw, code):
+    assert _mla(**kw) == code
+
+
+def test_validate_layout_rejects_bad_arguments():
+    assert LIB.csa_validate_layout(None, FAKE, 1, 0, 0, 0, -1, None) == EINVAL
+    assert LIB.csa_validate_layout(FAKE, FAKE, 0, 0, 0, 0, -1, None) == EINVAL
