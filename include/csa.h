@@ -35,6 +35,7 @@
  *   cu_seqlens_cmp[B]; rows at or past the true count are never written.
  * - dtype: CSA_BF16 (bfloat16 storage, fp32 accumulation) or CSA_F32.
  *   `sinks`, `lse` and `topk_score` are always float32; indices are int32.
+ * - A tensor argument whose governing size is zero (e.g. q when Tq == 0) may be NULL.
  * - Return value: CSA_OK or an error code.  All argument checks run on the host
  *   before any launch, so a failed call enqueues nothing and writes nothing.
  *   csa_last_error() returns the calling thread's last error message.

@@ -12,7 +12,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
+# CSA_LIBRARY may point at another build of the same library (e.g. a debug build).
+LIB_PATH = os.environ.get("CSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa.so")
 
 CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP = 0, 1, 2, 4
 CSA_F32, CSA_BF16 = 0, 1

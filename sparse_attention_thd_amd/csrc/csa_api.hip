@@ -70,7 +70,8 @@ int csa_build_indices(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
 int csa_compress(const void* x, int32_t Tkv, int32_t d, int32_t dtype, const int32_t* cu_seqlens_kv,
                  const int32_t* cu_seqlens_cmp, int32_t B, int32_t cmp_ratio, void* x_cmp, int32_t Tc_cap,
                  csa_stream_t stream) {
-  if (!x || !x_cmp || !cu_seqlens_kv || !cu_seqlens_cmp) return fail(CSA_EINVAL, "csa_compress: NULL pointer");
+  if (!cu_seqlens_kv || !cu_seqlens_cmp || (!x && Tkv > 0) || (!x_cmp && Tc_cap > 0))
+    return fail(CSA_EINVAL, "csa_compress: NULL pointer");
   if (B < 1 || Tkv < 0 || d < 1 || cmp_ratio < 1)
     return fail(CSA_EINVAL, "csa_compress: need B >= 1, Tkv >= 0, d >= 1, cmp_ratio >= 1");
   if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_compress: unknown dtype %d", dtype);
@@ -88,7 +89,8 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_
                      const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
                      int32_t max_seqlen_kv, int32_t topk, int32_t* topk_idx, float* topk_score,
                      csa_stream_t stream) {
-  if (!q_I || !w || !k_I_cmp || !topk_idx || !cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp)
+  if (!cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp || !k_I_cmp ||
+      (Tq != 0 && (!q_I || !w || !topk_idx)))
     return fail(CSA_EINVAL, "csa_indexer_topk: NULL pointer");
   if (B < 1 || Tq < 0 || H_I < 1 || d_I < 1 || topk < 1 || cmp_ratio < 1 || max_seqlen_kv < 0 || global_start < 0)
     return fail(CSA_EINVAL, "csa_indexer_topk: invalid size or parameter");
@@ -111,7 +113,7 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
                        const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp, int32_t B,
                        int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
                        const float* sinks, float softmax_scale, void* out, float* lse, csa_stream_t stream) {
-  if (!q || !ori_kv || !out || !cu_seqlens_q || !cu_seqlens_kv)
+  if (!cu_seqlens_q || !cu_seqlens_kv || !ori_kv || (Tq != 0 && (!q || !out)))
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: NULL pointer");
   if (cmp_kv && !cu_seqlens_cmp) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: cmp_kv needs cu_seqlens_cmp");
   if (cmp_idx && !cmp_kv) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: cmp_idx given without cmp_kv");

@@ -87,25 +87,94 @@ __device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const i
 
 // ----------------------------------------------------------------------------- MFMA path
 
-constexpr int kNT = 32;             // keys per tile
-constexpr int kStride = 512 + 8;    // LDS row stride in bf16 elements (1040 bytes)
+constexpr int kNT = 32;                      // keys per tile
+constexpr int kRowBytes = 1024;              // one latent row: 512 bf16
+constexpr int kTileBytes = kNT * kRowBytes;  // 32 KiB, two buffers in flight
 
-__global__ __launch_bounds__(kThreads) void mla_fwd_h64_d512_kernel(
+// 16-byte chunk q of tile row `row` lives at chunk q ^ swz(row).  Rows 0..15 get 16
+// distinct XOR values, so the 16 rows of a b128 K-fragment read hit 16 distinct
+// 16-byte bank groups, and rows 4g..4g+3 of a b64 transpose read keep their 32-byte
+// spans apart.
+__device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define CSA_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+// One 1 KiB row (64 lanes x 16 bytes) from global memory straight into LDS at byte
+// offset `lds_off` (wave-uniform).  Issued as inline asm so the compiler does not
+// treat the in-flight copy as a pending LDS write (it would drain the vector memory
+// counter before every LDS read); the caller waits on it with s_waitcnt vmcnt.
+__device__ __forceinline__ void row_to_lds(const void* gptr, uint32_t lds_off) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_off), "v"(gptr)
+      : "memory", "m0");
+}
+
+// Workgroup barrier without the full memory-counter drain that __syncthreads()
+// implies, so the next tile's global->LDS loads stay in flight across it.  The
+// empty asm keeps the compiler from moving LDS accesses across the barrier; the
+// caller waits for exactly the loads it needs with s_waitcnt.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x4 ds_read_tr(const unsigned char* p) {
+  return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4*)(p)));
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_fwd_h64_d512_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv,
-    const int32_t* __restrict__ cmp_idx, int topk, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cmp_idx, int topk, int Tq, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
     int wr, const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kNT * kStride];
+  __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
   __shared__ int32_t crow[kMaxTopk];
   __shared__ uint32_t wsum[kWaves];
 
-  const int i = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Blocks are dispatched round-robin over the 8 XCDs.  Each XCD takes runs of 8
+  // consecutive queries (which share window rows and compressed rows in its L2),
+  // and runs alternate between XCDs so long, expensive segments spread evenly.
+  const int kx = static_cast<int>(blockIdx.x >> 3);
+  const int i = ((kx >> 3) * 8 + static_cast<int>(blockIdx.x & 7u)) * 8 + (kx & 7);
+  if (i >= Tq) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const QueryKeys qk = query_keys(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr, cmp_idx,
                                   topk, crow, wsum);
   const int nkeys = qk.nwin + qk.ncmp;
+  const int ntiles = (nkeys + kNT - 1) / kNT;
+  const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
   const int head = 16 * wave + n;
+
+  // Stage tile t (32 rows) into buffer bf: wave w issues rows w, w+4, ..., one
+  // 1 KiB row per global_load_lds_dwordx4 (lane l fetches the chunk that lands at
+  // chunk l of the swizzled row).  Rows past the key list re-read a valid row; their
+  // probabilities are exactly zero.
+  auto issue = [&](int t, int bf) {
+#pragma unroll
+    for (int pass = 0; pass < kNT / kWaves; ++pass) {
+      const int rr = pass * kWaves + wave;
+      int kidx = t * kNT + rr;
+      kidx = (kidx < nkeys) ? kidx : 0;
+      const uint16_t* src;
+      if (kidx < qk.nwin) {
+        src = ori_kv + static_cast<long long>(qk.lo + kidx) * 512;
+      } else {
+        const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
+        src = cmp_kv + static_cast<long long>(c) * 512;
+      }
+      row_to_lds(src + ((lane ^ swz(rr)) << 3), kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowBytes));
+    }
+  };
+  if (ntiles > 0) issue(0, 0);
 
   // B operand of S^T = K . Q^T: lane (head n, group g) holds q[i, head, 32*ks + 8*g + 0..7]
   bf16x8 qf[16];
@@ -114,10 +183,13 @@ __global__ __launch_bounds__(kThreads) void mla_fwd_h64_d512_kernel(
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   }
+  // Drain here (tile 0 is needed first anyway) so that no compiler-placed wait for
+  // these loads lands inside the tile loop, where it would also drain the prefetch.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   f32x4 o[32];
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // running max in log2 units; the sink is the initial state (value 0, weight 1 counted once)
+  // Running max in log2 units; the sink is the initial state (value 0, weight 1 counted once).
   float m_run = -__builtin_huge_valf();
   float l_run = 0.f;
   if (sinks != nullptr) {
@@ -125,86 +197,80 @@ __global__ __launch_bounds__(kThreads) void mla_fwd_h64_d512_kernel(
     l_run = (g == 0) ? 1.f : 0.f;
   }
 
-  for (int t0 = 0; t0 < nkeys; t0 += kNT) {
-    // ---- stage 32 key rows (1 KiB each) into LDS; wave w loads rows w, w+4, ...
+  // per-lane LDS byte offsets inside a tile
+  const int vq = swz(n);  // rows n and 16 + n
+  int offq[4];
 #pragma unroll
-    for (int pass = 0; pass < kNT / kWaves; ++pass) {
-      const int rr = pass * kWaves + wave;
-      const int kidx = t0 + rr;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (kidx < nkeys) {
-        const uint16_t* src;
-        if (kidx < qk.nwin) {
-          src = ori_kv + static_cast<long long>(qk.lo + kidx) * 512;
-        } else {
-          const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
-          src = cmp_kv + static_cast<long long>(c) * 512;
-        }
-        v = reinterpret_cast<const uint4*>(src)[lane];
-      }
-      *reinterpret_cast<uint4*>(&kt[rr * kStride + lane * 8]) = v;
-    }
-    __syncthreads();
+  for (int k2 = 0; k2 < 4; ++k2) offq[k2] = n * kRowBytes + (((4 * k2 + g) ^ vq) << 4);
+  const int r1 = 4 * g + (n >> 2);  // transpose reads: rows r1 and r1 + 16
+  const int v1 = swz(r1);
+  const int c2 = (n & 3) >> 1, half = (n & 1) * 8;
+  int offv[8];
+#pragma unroll
+  for (int m3 = 0; m3 < 8; ++m3) offv[m3] = r1 * kRowBytes + ((((2 * m3) | c2) ^ v1) << 4) + half;
 
-    // ---- S^T = K . Q^T for keys [16*mb, 16*mb+16)
-    f32x4 s[2];
+  for (int t = 0; t < ntiles; ++t) {
+    const int bf = t & 1;
+    if (t + 1 < ntiles) {
+      issue(t + 1, bf ^ 1);
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt <= 8: this tile's rows have landed
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt == 0
+    }
+    tile_barrier();
+    const unsigned char* tb = kt + bf * kTileBytes;
+
+    // ---- S^T = K . Q^T for keys [0,16) and [16,32) of the tile
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[(16 * mb + n) * kStride + 32 * ks + 8 * g]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], acc, 0, 0, 0);
-      }
-      s[mb] = acc;
+    for (int ks = 0; ks < 16; ++ks) {
+      const unsigned char* pa = tb + offq[ks & 3] + 256 * (ks >> 2);
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(pa);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(pa + 16 * kRowBytes);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
     }
 
-    // ---- online softmax; lane holds keys 16*mb + 4*g + j of head `head`
+    // ---- online softmax; this lane holds keys 4g+j and 16+4g+j of head `head`
     float z[8];
     float tmax = -__builtin_huge_valf();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kidx = t0 + 16 * mb + 4 * g + j;
-        const float v = (kidx < nkeys) ? s[mb][j] * scale_log2 : -__builtin_huge_valf();
-        z[4 * mb + j] = v;
-        tmax = fmaxf(tmax, v);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = t * kNT + 4 * g + j;
+      z[j] = (k0 < nkeys) ? s0[j] * scale_log2 : -__builtin_huge_valf();
+      z[4 + j] = (k0 + 16 < nkeys) ? s1[j] * scale_log2 : -__builtin_huge_valf();
+      tmax = fmaxf(tmax, fmaxf(z[j], z[4 + j]));
+    }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -__builtin_huge_valf()) ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    // Lazy rescale: keep a stale maximum while the tile stays within 2^8 of it.
+    if (__any(tmax > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
+      m_run = m_new;
+    }
     bf16x8 pb;
-    float psum = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const __bf16 ph = static_cast<__bf16>(exp2f(z[j] - m_use));
-      pb[j] = ph;
-      psum += static_cast<float>(ph);
+      const float p = exp2f(z[j] - m_run);
+      l_run += p;
+      pb[j] = static_cast<__bf16>(p);
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
 
-    // ---- O^T += V^T . P^T; k-slot 8*g + j <-> key 4*g + j (j < 4) or 16 + 4*g + (j - 4)
+    // ---- O^T += V^T . P^T; k-slot 8g+j <-> key 4g+j (j < 4) or 16+4g+(j-4)
 #pragma unroll
     for (int mb = 0; mb < 32; ++mb) {
-      const int col = 16 * mb + n;
-      uint16_t e[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        e[j] = kt[(4 * g + j) * kStride + col];
-        e[4 + j] = kt[(16 + 4 * g + j) * kStride + col];
-      }
-      bf16x8 a;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a[j] = __builtin_bit_cast(__bf16, e[j]);
+      const unsigned char* pv = tb + offv[mb & 7] + 256 * (mb >> 3);
+      const bf16x4 lo4 = ds_read_tr(pv);
+      const bf16x4 hi4 = ds_read_tr(pv + 16 * kRowBytes);
+      const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
       o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mb], 0, 0, 0);
     }
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt == 0: this wave's LDS reads of the buffer are done
+    tile_barrier();
   }
 
   float l_tot = l_run;
@@ -319,8 +385,9 @@ hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_
   if (Tq <= 0) return hipSuccess;
   if (cmp_idx == nullptr) topk = 0;
   if (dtype == 1 && H == 64 && d == 512) {
-    hipLaunchKernelGGL(mla_fwd_h64_d512_kernel, dim3(Tq), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, cu_q,
+    const unsigned grid = static_cast<unsigned>((Tq + 63) / 64) * 64u;  // whole runs of 8 queries x 8 XCDs
+    hipLaunchKernelGGL(mla_fwd_h64_d512_kernel, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, Tq, cu_q,
                        cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale * kLog2e,
                        static_cast<uint16_t*>(out), lse);
     return hipGetLastError();
