@@ -90,6 +90,8 @@ __device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const i
 constexpr int kNT = 32;                      // keys per tile
 constexpr int kRowBytes = 1024;              // one latent row: 512 bf16
 constexpr int kTileBytes = kNT * kRowBytes;  // 32 KiB, two buffers in flight
+constexpr int kQD = 1;                       // K-fragment prefetch distance (MFMA pairs)
+constexpr int kVD = 4;                       // V^T-fragment prefetch distance (MFMAs)
 
 // 16-byte chunk q of tile row `row` lives at chunk q ^ swz(row).  Rows 0..15 get 16
 // distinct XOR values, so the 16 rows of a b128 K-fragment read hit 16 distinct
@@ -104,13 +106,13 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 // offset `lds_off` (wave-uniform).  Issued as inline asm so the compiler does not
 // treat the in-flight copy as a pending LDS write (it would drain the vector memory
 // counter before every LDS read); the caller waits on it with s_waitcnt vmcnt.
-__device__ __forceinline__ void row_to_lds(const void* gptr, uint32_t lds_off) {
+__device__ __forceinline__ void row_to_lds(const void* row_base, uint32_t lane_off, uint32_t lds_off) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
+      "global_load_lds_dwordx4 %1, %2"
       :
-      : "s"(lds_off), "v"(gptr)
+      : "s"(lds_off), "v"(lane_off), "s"(row_base)
       : "memory", "m0");
 }
 
@@ -122,6 +124,31 @@ __device__ __forceinline__ void tile_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+}
+
+// max / sum over the four lanes l, l^16, l^32, l^48 that hold one head's keys
+__device__ __forceinline__ float quad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// K fragment as two 8-byte LDS reads (lo: k-slots 0..3, hi: 4..7 of the lane group).
+// volatile keeps the pair from being fused into one ds_read2 (16 bytes per lane),
+// which is as slow as ds_read_b128.
+__device__ __forceinline__ bf16x8 kfrag(const unsigned char* tb, int off_lo, int off_hi) {
+  typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+  typedef const volatile __attribute__((address_space(3))) unsigned long long lds_u64;
+  const unsigned long long lo = *(lds_u64*)(tb + off_lo);
+  const unsigned long long hi = *(lds_u64*)(tb + off_hi);
+  return __builtin_bit_cast(bf16x8, u64x2{lo, hi});
 }
 
 __device__ __forceinline__ bf16x4 ds_read_tr(const unsigned char* p) {
@@ -154,34 +181,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
   const int head = 16 * wave + n;
 
-  // Stage tile t (32 rows) into buffer bf: wave w issues rows w, w+4, ..., one
-  // 1 KiB row per global_load_lds_dwordx4 (lane l fetches the chunk that lands at
-  // chunk l of the swizzled row).  Rows past the key list re-read a valid row; their
+  // Stage tile t (32 rows) into buffer bf: wave w issues rows w, w+4, ..., one 1 KiB
+  // row per global_load_lds_dwordx4.  Lane p < 8 first resolves the source address
+  // of row 4p + w (one LDS lookup for all of them); each load then takes it as a
+  // scalar base, and lane l fetches the 16-byte chunk that lands at chunk l of the
+  // swizzled row.  Rows past the key list re-read a valid row; their
   // probabilities are exactly zero.
+  const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
   auto issue = [&](int t, int bf) {
+    const int p = lane & 7;
+    int kidx = t * kNT + 4 * p + wave;
+    kidx = (kidx < nkeys) ? kidx : 0;
+    const uint16_t* src;
+    if (kidx < qk.nwin) {
+      src = ori_kv + static_cast<long long>(qk.lo + kidx) * 512;
+    } else {
+      const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
+      src = cmp_kv + static_cast<long long>(c) * 512;
+    }
+    const unsigned long long a = reinterpret_cast<unsigned long long>(src);
+    const uint32_t a_lo = static_cast<uint32_t>(a), a_hi = static_cast<uint32_t>(a >> 32);
 #pragma unroll
     for (int pass = 0; pass < kNT / kWaves; ++pass) {
       const int rr = pass * kWaves + wave;
-      int kidx = t * kNT + rr;
-      kidx = (kidx < nkeys) ? kidx : 0;
-      const uint16_t* src;
-      if (kidx < qk.nwin) {
-        src = ori_kv + static_cast<long long>(qk.lo + kidx) * 512;
-      } else {
-        const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
-        src = cmp_kv + static_cast<long long>(c) * 512;
-      }
-      row_to_lds(src + ((lane ^ swz(rr)) << 3), kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowBytes));
+      const unsigned long long base =
+          (static_cast<unsigned long long>(__builtin_amdgcn_readlane(a_hi, pass)) << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(a_lo, pass));
+      // lane chunk offset, recomputed here (volatile asm is not hoisted) so that eight
+      // loop-invariant offsets do not stay live across the tile loop
+      uint32_t lane_off;
+      asm volatile("v_xor_b32 %0, %1, %2" : "=v"(lane_off) : "s"(swz(rr) << 4), "v"(lane16));
+      row_to_lds(reinterpret_cast<const void*>(base), lane_off,
+                 kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowBytes));
     }
   };
   if (ntiles > 0) issue(0, 0);
 
-  // B operand of S^T = K . Q^T: lane (head n, group g) holds q[i, head, 32*ks + 8*g + 0..7]
+  // B operand of S^T = K . Q^T.  Within MFMA step ks, k-slot 8g + j of lane group g
+  // stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 + 4*g + (j - 4): the same
+  // permutation the K fragments use, chosen so each half is one conflict-free 8-byte
+  // LDS read (a 16-byte ds_read_b128 of the same data is several times slower).
   bf16x8 qf[16];
   {
-    const uint16_t* qrow = q + (static_cast<long long>(i) * 64 + head) * 512 + 8 * g;
+    const uint16_t* qrow = q + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 32 * ks);
+      const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 32 * ks + 16);
+      qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
   }
   // Drain here (tile 0 is needed first anyway) so that no compiler-placed wait for
   // these loads lands inside the tile loop, where it would also drain the prefetch.
@@ -199,9 +247,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // per-lane LDS byte offsets inside a tile
   const int vq = swz(n);  // rows n and 16 + n
-  int offq[4];
+  int offq[2][4];         // [half][ks & 3]: 8-byte pieces at dims 32ks + 4g (+16)
 #pragma unroll
-  for (int k2 = 0; k2 < 4; ++k2) offq[k2] = n * kRowBytes + (((4 * k2 + g) ^ vq) << 4);
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int k2 = 0; k2 < 4; ++k2)
+      offq[hf][k2] = n * kRowBytes + (((4 * k2 + 2 * hf + (g >> 1)) ^ vq) << 4) + (g & 1) * 8;
   const int r1 = 4 * g + (n >> 2);  // transpose reads: rows r1 and r1 + 16
   const int v1 = swz(r1);
   const int c2 = (n & 3) >> 1, half = (n & 1) * 8;
@@ -220,15 +271,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     tile_barrier();
     const unsigned char* tb = kt + bf * kTileBytes;
 
-    // ---- S^T = K . Q^T for keys [0,16) and [16,32) of the tile
+    // ---- S^T = K . Q^T for keys [0,16) and [16,32) of the tile; K fragments are
+    // staged kQD steps ahead and the order is pinned with scheduling fences.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    {
+      bf16x8 a0[kQD], a1[kQD];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const unsigned char* pa = tb + offq[ks & 3] + 256 * (ks >> 2);
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(pa);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(pa + 16 * kRowBytes);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
+      for (int ks = 0; ks < kQD; ++ks) {
+        a0[ks] = kfrag(tb, offq[0][ks & 3] + 256 * (ks >> 2), offq[1][ks & 3] + 256 * (ks >> 2));
+        a1[ks] = kfrag(tb + 16 * kRowBytes, offq[0][ks & 3] + 256 * (ks >> 2), offq[1][ks & 3] + 256 * (ks >> 2));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const int sl = ks % kQD;
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0[sl], qf[ks], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[sl], qf[ks], s1, 0, 0, 0);
+        if (ks + kQD < 16) {
+          const int kn = ks + kQD;
+          a0[sl] = kfrag(tb, offq[0][kn & 3] + 256 * (kn >> 2), offq[1][kn & 3] + 256 * (kn >> 2));
+          a1[sl] = kfrag(tb + 16 * kRowBytes, offq[0][kn & 3] + 256 * (kn >> 2), offq[1][kn & 3] + 256 * (kn >> 2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 
     // ---- online softmax; this lane holds keys 4g+j and 16+4g+j of head `head`
@@ -241,8 +305,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       z[4 + j] = (k0 + 16 < nkeys) ? s1[j] * scale_log2 : -__builtin_huge_valf();
       tmax = fmaxf(tmax, fmaxf(z[j], z[4 + j]));
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = quad_max(tmax);
     // Lazy rescale: keep a stale maximum while the tile stays within 2^8 of it.
     if (__any(tmax > m_run + 8.f)) {
       const float m_new = fmaxf(m_run, tmax);
@@ -255,27 +318,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     bf16x8 pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = exp2f(z[j] - m_run);
+      const float p = __builtin_amdgcn_exp2f(z[j] - m_run);
       l_run += p;
       pb[j] = static_cast<__bf16>(p);
     }
 
-    // ---- O^T += V^T . P^T; k-slot 8g+j <-> key 4g+j (j < 4) or 16+4g+(j-4)
+    // ---- O^T += V^T . P^T; k-slot 8g+j <-> key 4g+j (j < 4) or 16+4g+(j-4).  The V^T
+    // fragments (two transpose reads each) are staged kVD MFMAs ahead.
+    {
+      bf16x4 vlo[kVD], vhi[kVD];
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
-      const unsigned char* pv = tb + offv[mb & 7] + 256 * (mb >> 3);
-      const bf16x4 lo4 = ds_read_tr(pv);
-      const bf16x4 hi4 = ds_read_tr(pv + 16 * kRowBytes);
-      const bf16x8 a = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mb], 0, 0, 0);
+      for (int mb = 0; mb < kVD; ++mb) {
+        const unsigned char* pv = tb + offv[mb & 7] + 256 * (mb >> 3);
+        vlo[mb] = ds_read_tr(pv);
+        vhi[mb] = ds_read_tr(pv + 16 * kRowBytes);
+      }
+#pragma unroll
+      for (int mb = 0; mb < 32; ++mb) {
+        const int sl = mb % kVD;
+        const bf16x8 a = {vlo[sl][0], vlo[sl][1], vlo[sl][2], vlo[sl][3],
+                          vhi[sl][0], vhi[sl][1], vhi[sl][2], vhi[sl][3]};
+        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mb], 0, 0, 0);
+        if (mb + kVD < 32) {
+          const unsigned char* pv = tb + offv[(mb + kVD) & 7] + 256 * ((mb + kVD) >> 3);
+          vlo[sl] = ds_read_tr(pv);
+          vhi[sl] = ds_read_tr(pv + 16 * kRowBytes);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt == 0: this wave's LDS reads of the buffer are done
     tile_barrier();
   }
 
-  float l_tot = l_run;
-  l_tot += __shfl_xor(l_tot, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = quad_sum(l_run);
   const float inv = 1.f / l_tot;
   uint16_t* orow = out + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
 #pragma unroll
