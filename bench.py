@@ -25,7 +25,7 @@ METRIC = "CSA fwd tokens/s (indexer+top-k+sparse MLA), 16k THD pack; % MFMA peak
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 MLA_SRC = os.path.join(ROOT, "sparse_attention_thd_amd", "csrc", "csa_mla.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_mla_pack16k.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_mla_pack16k.txt")
 
 WORKLOAD_TEXT = {
     "pack16k": "16384-token THD pack (12 segments, lognormal(7,1) lengths, none a multiple of 4), 64 heads x "
@@ -106,9 +106,11 @@ def cpu_baseline(pack, budget_s=15.0):
     rng = np.random.default_rng(0)
     done, t_q = 0, 0.0
     chunk = 64
-    while t_q < budget_s and done < pack.Tq:
-        a = int(rng.integers(0, max(pack.Tq - chunk, 1)))
-        qs = list(range(a, min(a + chunk, pack.Tq)))
+    starts = rng.permutation(np.arange(0, pack.Tq, chunk))
+    for a in starts:
+        if t_q >= budget_s:
+            break
+        qs = list(range(int(a), min(int(a) + chunk, pack.Tq)))
         t1 = time.perf_counter()
         cmp_idx = None
         if mode == oracle.INDEXER:
@@ -127,7 +129,8 @@ def cpu_baseline(pack, budget_s=15.0):
         cores = 1
     return {"value": pack.Tq / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"layout + compression of the whole pack ({t_fixed:.1f} s), then indexer + attention for "
-                      f"{done} of {pack.Tq} queries in random 64-query chunks ({t_q:.1f} s), extrapolated per query"}
+                      f"{done} of {pack.Tq} queries in distinct random 64-query chunks ({t_q:.1f} s), "
+                      f"extrapolated per query to the whole pack"}
 
 
 def main():
@@ -139,6 +142,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design, "
@@ -146,6 +151,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device="cuda").fill_(1)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 2, "copy_calibration_bytes_written":
+                          dst.numel() * 2, "steps": max(args.steps, 1)}), flush=True)
+        return
     from synth import make_pack
     from sparse_attention_thd_amd import CsaPlan, ThdLayout
 
@@ -213,9 +227,12 @@ def main():
     idx_ms = float(t_idx.mean())
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
-        tr = json.load(open(TRAFFIC_FILE))
+        # "key: value" lines written from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes; the
+        # figure only counts while the kernel source is the one it was measured on
+        tr = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line and not line.startswith("#"))
+        tr = {k.strip(): v.strip() for k, v in tr.items()}
         if tr.get("kernel_source_sha256_16") == _sha(MLA_SRC) and tr.get("workload") == args.workload:
-            traffic = tr.get("hbm_bytes_per_launch")
+            traffic = float(tr["hbm_bytes_per_launch"])
     result = {
         "metric": METRIC,
         "value": tokens_s,
