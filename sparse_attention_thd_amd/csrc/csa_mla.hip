@@ -28,13 +28,22 @@ struct QueryKeys {
   int cmp_base;  // first visible row (attend-all mode)
 };
 
+// Workgroup barrier that only orders LDS traffic: it waits for this wavefront's
+// LDS operations but, unlike __syncthreads(), leaves global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt == 0
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Exclusive count of `f` over the block in thread order (block-uniform call).
 __device__ __forceinline__ uint32_t count_excl(bool f, uint32_t* wsum, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint64_t m = __ballot(f);
   const uint32_t in_wave = __popcll(m & ((1ull << lane) - 1ull));
   if (lane == 0) wsum[wave] = __popcll(m);
-  __syncthreads();
+  lds_barrier();
   uint32_t off = 0, tot = 0;
 #pragma unroll
   for (int k = 0; k < kWaves; ++k) {
@@ -42,19 +51,31 @@ __device__ __forceinline__ uint32_t count_excl(bool f, uint32_t* wsum, uint32_t&
     off += (k < wave) ? v : 0u;
     tot += v;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return off + in_wave;
 }
 
-// Resolve the query's window and compressed key ranges; in sparse mode compact
-// the valid entries of cmp_idx[i, :] (in their given order) into crow.
-__device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
-                                const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
-                                bool has_cmp, const int32_t* __restrict__ cmp_idx, int topk, int32_t* crow,
-                                uint32_t* wsum) {
+// Largest b in [0, B) with cu[b] <= x (cu non-decreasing, cu[0] <= x), found with
+// one wide load per 64 entries and a ballot instead of a chain of dependent loads.
+// The result is wave-uniform, so the loads that depend on it are scalar.
+__device__ __forceinline__ int segment_of_wave(const int32_t* __restrict__ cu, int B, int x) {
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < B; base += 64) {
+    const int k = base + lane;
+    const bool le = (k < B) && cu[k] <= x;
+    count += __popcll(__ballot(le));
+  }
+  return __builtin_amdgcn_readfirstlane(count - 1);
+}
+
+// Resolve the query's window and compressed key ranges.
+__device__ QueryKeys query_ranges(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+                                  const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
+                                  bool has_cmp, bool attend_all) {
   QueryKeys k;
-  const int b = segment_of(cu_q, B, i);
+  const int b = segment_of_wave(cu_q, B, i);
   const int t = global_start + i;
   const int s = cu_kv[b], e = cu_kv[b + 1];
   k.lo = max(s, t - wl);
@@ -62,26 +83,47 @@ __device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const i
   k.nwin = hi - k.lo + 1;
   k.ncmp = 0;
   k.cmp_base = cu_cmp[b];
-  if (!has_cmp) return k;
-  if (cmp_idx == nullptr) {
+  if (has_cmp && attend_all) {
     const int nv = (t - s + 1) / r;
     k.ncmp = max(0, min(nv, cu_cmp[b + 1] - k.cmp_base));
-    return k;
   }
-  const int Tc = cu_cmp[B];
-  const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
+  return k;
+}
+
+// Compact the valid entries of a cmp_idx row (in their given order) into crow;
+// `vals` holds this thread's entries j = threadIdx.x + kThreads * c.  Returns the count.
+template <int NC>
+__device__ int compact_rows(const int (&vals)[NC], int topk, int Tc, int32_t* crow, uint32_t* wsum) {
   uint32_t base = 0;
-  for (int j0 = 0; j0 < topk; j0 += kThreads) {
-    const int j = j0 + threadIdx.x;
-    const int c = (j < topk) ? row[j] : -1;
+#pragma unroll
+  for (int ch = 0; ch < NC; ++ch) {
+    if (ch * kThreads >= topk) break;
+    const int c = vals[ch];
     const bool ok = c >= 0 && c < Tc;  // entries outside the compressed rows are dropped
     uint32_t tot;
     const uint32_t pos = base + count_excl(ok, wsum, tot);
     if (ok) crow[pos] = c;
     base += tot;
   }
-  __syncthreads();
-  k.ncmp = static_cast<int>(base);
+  lds_barrier();
+  return static_cast<int>(base);
+}
+
+// Generic-path helper: ranges plus compaction, loading the cmp_idx row itself.
+__device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+                                const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
+                                bool has_cmp, const int32_t* __restrict__ cmp_idx, int topk, int32_t* crow,
+                                uint32_t* wsum) {
+  QueryKeys k = query_ranges(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, has_cmp, cmp_idx == nullptr);
+  if (!has_cmp || cmp_idx == nullptr) return k;
+  const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
+  int vals[kMaxTopk / kThreads];
+#pragma unroll
+  for (int ch = 0; ch < kMaxTopk / kThreads; ++ch) {
+    const int j = ch * kThreads + static_cast<int>(threadIdx.x);
+    vals[ch] = (j < topk) ? row[j] : -1;
+  }
+  k.ncmp = compact_rows(vals, topk, cu_cmp[B], crow, wsum);
   return k;
 }
 
@@ -156,6 +198,7 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const unsigned char* p) {
                                          (__attribute__((address_space(3))) s16x4*)(p)));
 }
 
+template <int NC>  // cmp_idx row chunks of kThreads entries: ceil(topk / 256)
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_fwd_h64_d512_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv,
     const int32_t* __restrict__ cmp_idx, int topk, int Tq, const int32_t* __restrict__ cu_q,
@@ -174,12 +217,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const QueryKeys qk = query_keys(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr, cmp_idx,
-                                  topk, crow, wsum);
+  const int head = 16 * wave + n;
+  const bool sparse = cmp_kv != nullptr && cmp_idx != nullptr;
+
+  // Prologue loads are issued cheapest-first and all stay in flight together; each
+  // later use waits only for the loads it needs (the counter retires them in order).
+  const int cu0 = (lane < B) ? cu_q[lane] : 0x7fffffff;  // first 64 segment starts
+  int vals[NC];
+  if (sparse) {
+    const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
+#pragma unroll
+    for (int ch = 0; ch < NC; ++ch) vals[ch] = row[min(ch * kThreads + tid, topk - 1)];
+  }
+  // B operand of S^T = K . Q^T.  Within MFMA step ks, k-slot 8g + j of lane group g
+  // stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 + 4*g + (j - 4): the same
+  // permutation the K fragments use, chosen so each half is one conflict-free 8-byte
+  // LDS read (a 16-byte ds_read_b128 of the same data is several times slower).
+  bf16x8 qf[16];
+  {
+    const uint16_t* qrow = q + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 32 * ks);
+      const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 32 * ks + 16);
+      qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+  }
+  // segment of query row i: count segment starts <= i (one ballot per 64 segments)
+  int count = __popcll(__ballot(cu0 <= i));
+  for (int base = 64; base < B; base += 64) count += __popcll(__ballot(base + lane < B && cu_q[base + lane] <= i));
+  const int b = __builtin_amdgcn_readfirstlane(count - 1);
+  QueryKeys qk;
+  {
+    const int t = global_start + i;
+    const int s = cu_kv[b], e = cu_kv[b + 1];
+    qk.lo = max(s, t - wl);
+    qk.nwin = min(e - 1, t + wr) - qk.lo + 1;
+    qk.cmp_base = cu_cmp[b];
+    qk.ncmp = 0;
+    if (cmp_kv != nullptr && cmp_idx == nullptr)
+      qk.ncmp = max(0, min((t - s + 1) / r, cu_cmp[b + 1] - qk.cmp_base));
+  }
+  if (sparse) {
+#pragma unroll
+    for (int ch = 0; ch < NC; ++ch) vals[ch] = (ch * kThreads + tid < topk) ? vals[ch] : -1;
+    qk.ncmp = compact_rows(vals, topk, cu_cmp[B], crow, wsum);
+  }
   const int nkeys = qk.nwin + qk.ncmp;
   const int ntiles = (nkeys + kNT - 1) / kNT;
   const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
-  const int head = 16 * wave + n;
 
   // Stage tile t (32 rows) into buffer bf: wave w issues rows w, w+4, ..., one 1 KiB
   // row per global_load_lds_dwordx4.  Lane p < 8 first resolves the source address
@@ -217,20 +303,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   };
   if (ntiles > 0) issue(0, 0);
 
-  // B operand of S^T = K . Q^T.  Within MFMA step ks, k-slot 8g + j of lane group g
-  // stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 + 4*g + (j - 4): the same
-  // permutation the K fragments use, chosen so each half is one conflict-free 8-byte
-  // LDS read (a 16-byte ds_read_b128 of the same data is several times slower).
-  bf16x8 qf[16];
-  {
-    const uint16_t* qrow = q + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 32 * ks);
-      const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 32 * ks + 16);
-      qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-    }
-  }
   // Drain here (tile 0 is needed first anyway) so that no compiler-placed wait for
   // these loads lands inside the tile loop, where it would also drain the prefetch.
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -353,14 +425,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   const float l_tot = quad_sum(l_run);
   const float inv = 1.f / l_tot;
-  uint16_t* orow = out + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
+  // Stage this wavefront's 16 head rows through its quarter of the (now idle) tile
+  // buffers so the output leaves as one contiguous 1 KiB row per store instruction.
+  // Row n, 16-byte chunk c lives at chunk c ^ swz(n), as in the tiles.
+  unsigned char* stage = kt + wave * (16 * kRowBytes);
+  // Lane-derived offsets are recomputed from an opaque copy of the lane id so the
+  // compiler does not hoist them above the tile loop (where they would spill).
+  int el;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
+  const int en = el & 15, eg = el >> 4;
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) {
     const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0] * inv)) |
                         (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1] * inv)) << 16);
     const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2] * inv)) |
                         (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3] * inv)) << 16);
-    *reinterpret_cast<uint2*>(orow + 16 * mb) = make_uint2(w0, w1);
+    const int chunk = (2 * mb + (eg >> 1)) ^ swz(en);
+    *reinterpret_cast<uint2*>(stage + en * kRowBytes + chunk * 16 + (eg & 1) * 8) = make_uint2(w0, w1);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's staging writes are done
+  uint16_t* obase = out + (static_cast<long long>(i) * 64 + 16 * wave) * 512;
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + h * kRowBytes + ((el ^ swz(h)) << 4));
+    *reinterpret_cast<uint4*>(obase + h * 512 + el * 8) = v;
   }
   if (lse != nullptr && g == 0) lse[static_cast<long long>(i) * 64 + head] = m_run * kLn2 + logf(l_tot);
 }
@@ -462,7 +550,8 @@ hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_
   if (cmp_idx == nullptr) topk = 0;
   if (dtype == 1 && H == 64 && d == 512) {
     const unsigned grid = static_cast<unsigned>((Tq + 63) / 64) * 64u;  // whole runs of 8 queries x 8 XCDs
-    hipLaunchKernelGGL(mla_fwd_h64_d512_kernel, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
+    auto kern = (topk <= 2 * kThreads) ? mla_fwd_h64_d512_kernel<2> : mla_fwd_h64_d512_kernel<kMaxTopk / kThreads>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, Tq, cu_q,
                        cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale * kLog2e,
                        static_cast<uint16_t*>(out), lse);
