@@ -334,13 +334,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   for (int t = 0; t < ntiles; ++t) {
     const int bf = t & 1;
-    if (t + 1 < ntiles) {
-      issue(t + 1, bf ^ 1);
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt <= 8: this tile's rows have landed
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt == 0
-    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wavefront's rows of tile t have landed
+    // The barrier publishes every wavefront's rows of tile t, and it also means all
+    // of them are done reading buffer bf ^ 1 (tile t - 1), which the next loads refill.
     tile_barrier();
+    if (t + 1 < ntiles) issue(t + 1, bf ^ 1);
     const unsigned char* tb = kt + bf * kTileBytes;
 
     // ---- S^T = K . Q^T for keys [0,16) and [16,32) of the tile; K fragments are
@@ -419,8 +417,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt == 0: this wave's LDS reads of the buffer are done
-    tile_barrier();
   }
 
   const float l_tot = quad_sum(l_run);
@@ -428,6 +424,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // Stage this wavefront's 16 head rows through its quarter of the (now idle) tile
   // buffers so the output leaves as one contiguous 1 KiB row per store instruction.
   // Row n, 16-byte chunk c lives at chunk c ^ swz(n), as in the tiles.
+  tile_barrier();  // every wavefront is done reading the last tile
   unsigned char* stage = kt + wave * (16 * kRowBytes);
   // Lane-derived offsets are recomputed from an opaque copy of the lane id so the
   // compiler does not hoist them above the tile loop (where they would spill).
