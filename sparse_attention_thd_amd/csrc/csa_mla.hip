@@ -82,7 +82,7 @@ __device__ QueryKeys query_ranges(int i, const int32_t* __restrict__ cu_q, const
   const int hi = min(e - 1, t + wr);
   k.nwin = hi - k.lo + 1;
   k.ncmp = 0;
-  k.cmp_base = cu_cmp[b];
+  k.cmp_base = (cu_cmp != nullptr) ? cu_cmp[b] : 0;
   if (has_cmp && attend_all) {
     const int nv = (t - s + 1) / r;
     k.ncmp = max(0, min(nv, cu_cmp[b + 1] - k.cmp_base));
@@ -131,14 +131,20 @@ __device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const i
 
 constexpr int kNT = 32;                      // keys per tile
 constexpr int kRowBytes = 1024;              // one latent row: 512 bf16
-constexpr int kTileBytes = kNT * kRowBytes;  // 32 KiB, two buffers in flight
-constexpr int kQD = 1;                       // K-fragment prefetch distance (MFMA pairs)
+constexpr int kRowStride = kRowBytes + 16;   // padded tile row, see kpi()
+constexpr int kTileBytes = kNT * kRowStride; // 32.5 KiB, two buffers in flight
+constexpr int kQD = 2;                       // K-fragment prefetch distance (MFMA pairs)
 constexpr int kVD = 4;                       // V^T-fragment prefetch distance (MFMAs)
 
-// 16-byte chunk q of tile row `row` lives at chunk q ^ swz(row).  Rows 0..15 get 16
-// distinct XOR values, so the 16 rows of a b128 K-fragment read hit 16 distinct
-// 16-byte bank groups, and rows 4g..4g+3 of a b64 transpose read keep their 32-byte
-// spans apart.
+// Tile rows are padded to 1040 bytes, so row r starts 4 banks (of 64 x 4 bytes) after
+// row r - 1, and every fragment read is a per-lane base plus an immediate offset.
+// The 16 K rows of an S^T MFMA are taken in the order kpi(0..15) = 0, 2, .., 14, 1,
+// 3, .., 15 (accumulator row k holds key kpi(k)).  Then a b64 K read (16 rows x 16
+// bytes per half-wavefront) and a transpose V read (rows kpi(0..7) or kpi(8..15),
+// 32 bytes each, per half-wavefront) both touch each bank once.
+__device__ __forceinline__ int kpi(int k) { return ((k & 7) << 1) | (k >> 3); }
+
+// Output staging (1 KiB rows): 16-byte chunk q of row `row` lives at chunk q ^ swz(row).
 __device__ __forceinline__ int swz(int row) { return ((row & 7) << 1) | ((row >> 3) & 1); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -222,7 +228,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   // Prologue loads are issued cheapest-first and all stay in flight together; each
   // later use waits only for the loads it needs (the counter retires them in order).
+  // With B < 64 every lane b <= B also fetches cu_kv[b] and cu_cmp[b], so the segment's
+  // bounds come from a register broadcast instead of a second dependent load.
+  const bool small_b = B < 64;
   const int cu0 = (lane < B) ? cu_q[lane] : 0x7fffffff;  // first 64 segment starts
+  const int kv0 = (small_b && lane <= B) ? cu_kv[lane] : 0;
+  const int cm0 = (small_b && lane <= B && cu_cmp != nullptr) ? cu_cmp[lane] : 0;
   int vals[NC];
   if (sparse) {
     const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
@@ -248,32 +259,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   for (int base = 64; base < B; base += 64) count += __popcll(__ballot(base + lane < B && cu_q[base + lane] <= i));
   const int b = __builtin_amdgcn_readfirstlane(count - 1);
   QueryKeys qk;
+  int cmp_end = 0, cmp_total = 0;  // cu_cmp[b + 1], cu_cmp[B]
+  const int t_abs = global_start + i;
+  int seg_s;
   {
-    const int t = global_start + i;
-    const int s = cu_kv[b], e = cu_kv[b + 1];
-    qk.lo = max(s, t - wl);
-    qk.nwin = min(e - 1, t + wr) - qk.lo + 1;
-    qk.cmp_base = cu_cmp[b];
+    int e;
+    if (small_b) {
+      seg_s = __builtin_amdgcn_readlane(kv0, b);
+      e = __builtin_amdgcn_readlane(kv0, b + 1);
+      qk.cmp_base = __builtin_amdgcn_readlane(cm0, b);
+      cmp_end = __builtin_amdgcn_readlane(cm0, b + 1);
+      cmp_total = __builtin_amdgcn_readlane(cm0, B);
+    } else {
+      seg_s = cu_kv[b];
+      e = cu_kv[b + 1];
+      if (cu_cmp != nullptr) {
+        qk.cmp_base = cu_cmp[b];
+        cmp_end = cu_cmp[b + 1];
+        cmp_total = cu_cmp[B];
+      } else {
+        qk.cmp_base = 0;
+      }
+    }
+    qk.lo = max(seg_s, t_abs - wl);
+    qk.nwin = min(e - 1, t_abs + wr) - qk.lo + 1;
     qk.ncmp = 0;
-    if (cmp_kv != nullptr && cmp_idx == nullptr)
-      qk.ncmp = max(0, min((t - s + 1) / r, cu_cmp[b + 1] - qk.cmp_base));
+    if (cmp_kv != nullptr && cmp_idx == nullptr) qk.ncmp = max(0, min((t_abs - seg_s + 1) / r, cmp_end - qk.cmp_base));
+  }
+  const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
+  const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
+  // Tile 0 is all window rows when the window has at least a tile of them; then it is
+  // issued here, so its latency overlaps the wait for the cmp_idx row.
+  const bool early_tile0 = qk.nwin >= kNT;
+  if (early_tile0) {
+    const uint16_t* src = ori_kv + static_cast<long long>(qk.lo + 4 * (lane & 7) + wave) * 512;
+    const unsigned long long a = reinterpret_cast<unsigned long long>(src);
+    const uint32_t a_lo = static_cast<uint32_t>(a), a_hi = static_cast<uint32_t>(a >> 32);
+#pragma unroll
+    for (int pass = 0; pass < kNT / kWaves; ++pass) {
+      const unsigned long long base = (static_cast<unsigned long long>(__builtin_amdgcn_readlane(a_hi, pass)) << 32) |
+                                      static_cast<uint32_t>(__builtin_amdgcn_readlane(a_lo, pass));
+      row_to_lds(reinterpret_cast<const void*>(base), lane16,
+                 kt_base + static_cast<uint32_t>((pass * kWaves + wave) * kRowStride));
+    }
   }
   if (sparse) {
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) vals[ch] = (ch * kThreads + tid < topk) ? vals[ch] : -1;
-    qk.ncmp = compact_rows(vals, topk, cu_cmp[B], crow, wsum);
+    qk.ncmp = compact_rows(vals, topk, cmp_total, crow, wsum);
   }
   const int nkeys = qk.nwin + qk.ncmp;
   const int ntiles = (nkeys + kNT - 1) / kNT;
-  const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
 
   // Stage tile t (32 rows) into buffer bf: wave w issues rows w, w+4, ..., one 1 KiB
   // row per global_load_lds_dwordx4.  Lane p < 8 first resolves the source address
   // of row 4p + w (one LDS lookup for all of them); each load then takes it as a
   // scalar base, and lane l fetches the 16-byte chunk that lands at chunk l of the
-  // swizzled row.  Rows past the key list re-read a valid row; their
+  // row.  Rows past the key list re-read a valid row; their
   // probabilities are exactly zero.
-  const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
   auto issue = [&](int t, int bf) {
     const int p = lane & 7;
     int kidx = t * kNT + 4 * p + wave;
@@ -293,15 +336,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       const unsigned long long base =
           (static_cast<unsigned long long>(__builtin_amdgcn_readlane(a_hi, pass)) << 32) |
           static_cast<uint32_t>(__builtin_amdgcn_readlane(a_lo, pass));
-      // lane chunk offset, recomputed here (volatile asm is not hoisted) so that eight
-      // loop-invariant offsets do not stay live across the tile loop
-      uint32_t lane_off;
-      asm volatile("v_xor_b32 %0, %1, %2" : "=v"(lane_off) : "s"(swz(rr) << 4), "v"(lane16));
-      row_to_lds(reinterpret_cast<const void*>(base), lane_off,
-                 kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowBytes));
+      row_to_lds(reinterpret_cast<const void*>(base), lane16,
+                 kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
     }
   };
-  if (ntiles > 0) issue(0, 0);
+  if (ntiles > 0 && !early_tile0) issue(0, 0);
 
   // Drain here (tile 0 is needed first anyway) so that no compiler-placed wait for
   // these loads lands inside the tile loop, where it would also drain the prefetch.
@@ -317,20 +356,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     l_run = (g == 0) ? 1.f : 0.f;
   }
 
-  // per-lane LDS byte offsets inside a tile
-  const int vq = swz(n);  // rows n and 16 + n
-  int offq[2][4];         // [half][ks & 3]: 8-byte pieces at dims 32ks + 4g (+16)
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-    for (int k2 = 0; k2 < 4; ++k2)
-      offq[hf][k2] = n * kRowBytes + (((4 * k2 + 2 * hf + (g >> 1)) ^ vq) << 4) + (g & 1) * 8;
-  const int r1 = 4 * g + (n >> 2);  // transpose reads: rows r1 and r1 + 16
-  const int v1 = swz(r1);
-  const int c2 = (n & 3) >> 1, half = (n & 1) * 8;
-  int offv[8];
-#pragma unroll
-  for (int m3 = 0; m3 < 8; ++m3) offv[m3] = r1 * kRowBytes + ((((2 * m3) | c2) ^ v1) << 4) + half;
+  // per-lane LDS byte offsets inside a tile: K reads of row kpi(n) at dims 32ks + 4g
+  // (+16); transpose V reads of row kpi(4g + n/4) at dims 16mb + 4(n%4)
+  const int offq = kpi(n) * kRowStride + 8 * g;
+  const int offv = kpi(4 * g + (n >> 2)) * kRowStride + 8 * (n & 3);
 
   for (int t = 0; t < ntiles; ++t) {
     const int bf = t & 1;
@@ -348,8 +377,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       bf16x8 a0[kQD], a1[kQD];
 #pragma unroll
       for (int ks = 0; ks < kQD; ++ks) {
-        a0[ks] = kfrag(tb, offq[0][ks & 3] + 256 * (ks >> 2), offq[1][ks & 3] + 256 * (ks >> 2));
-        a1[ks] = kfrag(tb + 16 * kRowBytes, offq[0][ks & 3] + 256 * (ks >> 2), offq[1][ks & 3] + 256 * (ks >> 2));
+        a0[ks] = kfrag(tb, offq + 64 * ks, offq + 64 * ks + 32);
+        a1[ks] = kfrag(tb + 16 * kRowStride, offq + 64 * ks, offq + 64 * ks + 32);
       }
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
@@ -358,8 +387,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[sl], qf[ks], s1, 0, 0, 0);
         if (ks + kQD < 16) {
           const int kn = ks + kQD;
-          a0[sl] = kfrag(tb, offq[0][kn & 3] + 256 * (kn >> 2), offq[1][kn & 3] + 256 * (kn >> 2));
-          a1[sl] = kfrag(tb + 16 * kRowBytes, offq[0][kn & 3] + 256 * (kn >> 2), offq[1][kn & 3] + 256 * (kn >> 2));
+          a0[sl] = kfrag(tb, offq + 64 * kn, offq + 64 * kn + 32);
+          a1[sl] = kfrag(tb + 16 * kRowStride, offq + 64 * kn, offq + 64 * kn + 32);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -370,7 +399,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     float tmax = -__builtin_huge_valf();
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int k0 = t * kNT + 4 * g + j;
+      const int k0 = t * kNT + kpi(4 * g + j);
       z[j] = (k0 < nkeys) ? s0[j] * scale_log2 : -__builtin_huge_valf();
       z[4 + j] = (k0 + 16 < nkeys) ? s1[j] * scale_log2 : -__builtin_huge_valf();
       tmax = fmaxf(tmax, fmaxf(z[j], z[4 + j]));
@@ -399,9 +428,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       bf16x4 vlo[kVD], vhi[kVD];
 #pragma unroll
       for (int mb = 0; mb < kVD; ++mb) {
-        const unsigned char* pv = tb + offv[mb & 7] + 256 * (mb >> 3);
+        const unsigned char* pv = tb + offv + 32 * mb;
         vlo[mb] = ds_read_tr(pv);
-        vhi[mb] = ds_read_tr(pv + 16 * kRowBytes);
+        vhi[mb] = ds_read_tr(pv + 16 * kRowStride);
       }
 #pragma unroll
       for (int mb = 0; mb < 32; ++mb) {
@@ -410,9 +439,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                           vhi[sl][0], vhi[sl][1], vhi[sl][2], vhi[sl][3]};
         o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mb], 0, 0, 0);
         if (mb + kVD < 32) {
-          const unsigned char* pv = tb + offv[(mb + kVD) & 7] + 256 * ((mb + kVD) >> 3);
+          const unsigned char* pv = tb + offv + 32 * (mb + kVD);
           vlo[sl] = ds_read_tr(pv);
-          vhi[sl] = ds_read_tr(pv + 16 * kRowBytes);
+          vhi[sl] = ds_read_tr(pv + 16 * kRowStride);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -423,7 +452,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float inv = 1.f / l_tot;
   // Stage this wavefront's 16 head rows through its quarter of the (now idle) tile
   // buffers so the output leaves as one contiguous 1 KiB row per store instruction.
-  // Row n, 16-byte chunk c lives at chunk c ^ swz(n), as in the tiles.
+  // Row n, 16-byte chunk c lives at chunk c ^ swz(n).
   tile_barrier();  // every wavefront is done reading the last tile
   unsigned char* stage = kt + wave * (16 * kRowBytes);
   // Lane-derived offsets are recomputed from an opaque copy of the lane id so the

@@ -38,6 +38,8 @@ def _small(name):
         return pack_from_lengths("win_right", [300, 411], seed=9, ori_win_left=20, ori_win_right=5, topk=32)
     if name == "no_compress":
         return pack_from_lengths("no_compress", [200, 333], seed=10, cmp_ratio=1, indexer=False)
+    if name == "many_segs":    # more than 64 segments (segment search and bounds past one wavefront)
+        return pack_from_lengths("many_segs", [5 + (37 * k) % 120 for k in range(80)], seed=13, topk=32)
     if name == "generic_f32":
         return pack_from_lengths("generic_f32", [5, 77, 140], seed=11, dtype="f32", H=4, d=64, H_I=2, d_I=32,
                                  ori_win_left=15, topk=8, q_scale=1.0, kv_scale=1.0, w_scale=2 ** -0.5,
@@ -50,7 +52,7 @@ def _small(name):
 
 FULL = ["tiny", "single4k", "pack16k", "hca32k", "cp32k", "stress"]
 SMALL = ["edges", "select16", "long", "short_only", "hca_small", "cp_small", "win_right", "no_compress",
-         "generic_f32", "generic_bf16"]
+         "many_segs", "generic_f32", "generic_bf16"]
 ALL = SMALL + FULL
 
 _cache = {}
@@ -148,6 +150,29 @@ def test_attention_matches_oracle(name):
     msg = assert_out_close(res["out"][qs], out, fp32=(pack.dtype == "f32"))
     print(f"[case] {name}: {len(qs)} queries; {msg}")
     assert np.abs(res["lse"][qs] - lse).max() <= LSE_ABS
+
+
+@pytest.mark.parametrize("name", ["no_compress", "edges", "generic_bf16"])
+def test_window_only_call_without_compressed_arrays(name):
+    """Window branch alone through the C ABI, with cmp_kv, cmp_idx and cu_seqlens_cmp all NULL."""
+    import sparse_attention_thd_amd as s
+    res = result(name)
+    pack, tabs = res["pack"], res["tabs"]
+    print(f"[case] {name}: window-only csa_sparse_mla_fwd, NULL compressed arrays", flush=True)
+    dt = torch.bfloat16 if pack.dtype == "bf16" else torch.float32
+    out = torch.empty((pack.Tq, pack.H, pack.d), dtype=dt, device="cuda")
+    lse = torch.empty((pack.Tq, pack.H), dtype=torch.float32, device="cuda")
+    s.csa_sparse_mla_fwd(to_device(pack.q), to_device(pack.ori_kv), None, None, 0, pack.Tq, pack.Tkv, pack.H,
+                         pack.d, torch.as_tensor(np.asarray(pack.cu_seqlens_q), dtype=torch.int32, device="cuda"),
+                         torch.as_tensor(np.asarray(pack.cu_seqlens_kv), dtype=torch.int32, device="cuda"), None, pack.B,
+                         pack.global_start, pack.cmp_ratio, pack.ori_win_left, pack.ori_win_right,
+                         to_device(pack.sinks), pack.softmax_scale, out, lse)
+    torch.cuda.synchronize()
+    qs = _queries(res)
+    ref, ref_lse = oracle_attention(pack, tabs, qs, None, None, oracle.NO_COMPRESS)
+    msg = assert_out_close(cpu(out)[qs], ref, fp32=(pack.dtype == "f32"))
+    print(f"[case] {name}: {len(qs)} queries; {msg}")
+    assert np.abs(cpu(lse)[qs] - ref_lse).max() <= LSE_ABS
 
 
 def test_end_to_end_equals_oracle_selection_on_small_pack():
