@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
 
-    // ---- online softmax; this lane holds keys 4g+j and 16+4g+j of head `head`
+    // ---- online softmax; this lane holds keys kpi(4g+j) and 16+kpi(4g+j) of head `head`
     float z[8];
     float tmax = -__builtin_huge_valf();
 #pragma unroll
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       pb[j] = static_cast<__bf16>(p);
     }
 
-    // ---- O^T += V^T . P^T; k-slot 8g+j <-> key 4g+j (j < 4) or 16+4g+(j-4).  The V^T
+    // ---- O^T += V^T . P^T; k-slot 8g+j <-> key kpi(4g+j) (j < 4) or 16+kpi(4g+j-4).  The V^T
     // fragments (two transpose reads each) are staged kVD MFMAs ahead.
     {
       bf16x4 vlo[kVD], vhi[kVD];
