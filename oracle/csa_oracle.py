@@ -14,7 +14,7 @@ Pages cited (by title; section names as they appear on the page):
         风险与影响.
 * [HP]  "【RFC】DeepSeek-V4 CSA/HCA 自定义算子接入与对外接口对标 torch_extension",
         sections 背景, 1. npu_lightning_indexer, 2. npu_sparse_flash_mla,
-        缺失入参的用途分析（对照实验）.
+        4. npu_sparse_flash_mla_grad, 缺失入参的用途分析（对照实验）.
 * [ML]  "feat(deepseek_v4): faithful THD context-parallel path for DS4 CSA
         (bounded activation memory)", sections What, Design, GPU verification.
 
@@ -36,6 +36,13 @@ design notes with its support):
   the lower row; result rows ascending, padded with -1.
 * one joint softmax over window rows, selected compressed rows and a per-head
   sink logit (not scaled by softmax_scale) with a zero value; K = V = the latent row.
+
+Backward (sparse_mla_bwd): the exact gradients of that forward for a given dout,
+with K = V, so a latent row's gradient is its key gradient plus its value gradient;
+the sink receives -sum_i p_sink * D.  The two "softmax_l1_norm" outputs are the
+attention probabilities averaged over the heads, per (query, key slot): window
+slot k is stream row lo + k (win_idx order), compressed slot j is the j-th attended
+compressed row in the order the forward lists them; unused slots hold 0.
 
 "parity unpinned": ``ori_win_right > 0`` (clamped at the segment end) has no
 independent pin; every other function is pinned in ``tests/test_oracle_pins.py``.
@@ -289,6 +296,95 @@ def sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, tables, sinks, softmax_scale,
         out[n] = (e @ K) / den[:, None]
         lse[n] = m + np.log(den)
     return out, lse
+
+
+def _query_keys(i, tables, ori_win_left, ori_win_right, cu_kv, global_start, cmp_idx, attend_all_visible,
+                cmp_present):
+    """Key list of query i in the forward's order: window rows, then compressed rows."""
+    b = int(tables["q_seg"][i])
+    t = int(global_start) + i
+    lo = max(cu_kv[b], t - int(ori_win_left))
+    hi = min(cu_kv[b + 1] - 1, t + int(ori_win_right))
+    rows = []
+    if cmp_present:
+        if attend_all_visible:
+            c0 = int(tables["q_cmp_lo"][i])
+            rows = list(range(c0, c0 + int(tables["q_cmp_nvis"][i])))
+        elif cmp_idx is not None:
+            rows = [int(c) for c in cmp_idx[i] if c >= 0]
+    return lo, hi, rows
+
+
+def sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, tables, sinks, softmax_scale, ori_win_left, ori_win_right,
+                   cu_seqlens_kv, global_start, dout, cmp_slots=0, attend_all_visible=False, queries=None):
+    """Gradients of sparse_mla_fwd for the output gradient ``dout``.
+
+    [HP] 4. npu_sparse_flash_mla_grad: the backward of the sparse MLA operator takes
+    q, dout, the forward output and lse plus the forward's key sources, and returns
+    d_query, d_ori_kv, d_cmp_kv, d_sinks and the window / compressed
+    "softmax_l1_norm" (the head-averaged attention distribution, shaped like the
+    index lists).  Written from the forward's definition (one joint softmax over
+    window rows, compressed rows and the sink; K = V):
+        P[h,k] = exp(z[h,k] - lse[h]),  z = scale * q[h] . kv[k],  p_sink = exp(sink[h] - lse[h])
+        dP[h,k] = dout[h] . kv[k],  D[h] = sum_k P[h,k] dP[h,k] = dout[h] . out[h]
+        dS[h,k] = P[h,k] (dP[h,k] - D[h])
+        dq[h] = scale * sum_k dS[h,k] kv[k]
+        dkv[k] += sum_h (scale * dS[h,k] q[h] + P[h,k] dout[h])
+        dsink[h] += -p_sink[h] D[h]
+    out and lse are recomputed here in fp64 (the operator receives them from the
+    forward).  Returns float64 arrays: dq [nq, H, d], d_ori_kv [Tkv, d],
+    d_cmp_kv [Tc, d] (None without compressed rows), d_sinks [H] (None without
+    sinks), ori_l1 [nq, W], cmp_l1 [nq, cmp_slots].  With ``queries`` only those
+    rows contribute (the kv gradients are then partial sums).
+    """
+    Tq = len(tables["q_seg"])
+    qs = range(Tq) if queries is None else list(queries)
+    nq = len(qs)
+    H, d = np.asarray(q[0]).shape if Tq else (0, 0)
+    W = int(ori_win_left) + int(ori_win_right) + 1
+    cu_kv = [int(v) for v in cu_seqlens_kv]
+    sk = None if sinks is None else np.asarray(sinks, dtype=np.float64)
+    dq = np.zeros((nq, H, d), dtype=np.float64)
+    d_ori = np.zeros((len(ori_kv), d), dtype=np.float64)
+    d_cmp = None if cmp_kv is None else np.zeros((len(cmp_kv), d), dtype=np.float64)
+    d_sinks = None if sk is None else np.zeros(H, dtype=np.float64)
+    ori_l1 = np.zeros((nq, W), dtype=np.float64)
+    cmp_l1 = np.zeros((nq, int(cmp_slots)), dtype=np.float64)
+    for n, i in enumerate(qs):
+        lo, hi, rows = _query_keys(i, tables, ori_win_left, ori_win_right, cu_kv, global_start, cmp_idx,
+                                   attend_all_visible, cmp_kv is not None)
+        nwin = hi - lo + 1
+        parts = [np.asarray(ori_kv[lo:hi + 1], dtype=np.float64)]
+        if rows:
+            parts.append(np.asarray(cmp_kv[rows], dtype=np.float64))
+        K = np.concatenate(parts, axis=0)             # [n_keys, d]; K = V
+        qi = np.asarray(q[i], dtype=np.float64)       # [H, d]
+        do = np.asarray(dout[n], dtype=np.float64)    # [H, d]
+        z = softmax_scale * (qi @ K.T)                # [H, n_keys]
+        m = z.max(axis=1)
+        if sk is not None:
+            m = np.maximum(m, sk)
+        den = np.exp(z - m[:, None]).sum(axis=1)
+        if sk is not None:
+            den = den + np.exp(sk - m)
+        lse = m + np.log(den)
+        P = np.exp(z - lse[:, None])                  # [H, n_keys]
+        out = P @ K                                   # [H, d]
+        dP = do @ K.T                                 # [H, n_keys]
+        D = (do * out).sum(axis=1)                    # [H]
+        dS = P * (dP - D[:, None])
+        dq[n] = softmax_scale * (dS @ K)
+        dK = softmax_scale * (dS.T @ qi) + P.T @ do   # [n_keys, d]
+        d_ori[lo:hi + 1] += dK[:nwin]
+        for j, c in enumerate(rows):
+            d_cmp[c] += dK[nwin + j]
+        if sk is not None:
+            d_sinks += -np.exp(sk - lse) * D
+        l1 = P.mean(axis=0)
+        ori_l1[n, :nwin] = l1[:nwin]
+        ncs = min(len(rows), int(cmp_slots))
+        cmp_l1[n, :ncs] = l1[nwin:nwin + ncs]
+    return dict(dq=dq, d_ori_kv=d_ori, d_cmp_kv=d_cmp, d_sinks=d_sinks, ori_l1=ori_l1, cmp_l1=cmp_l1)
 
 
 # --------------------------------------------------------------------------- forward
