@@ -184,6 +184,49 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
                        csa_stream_t stream);
 
 /*
+ * csa_sparse_mla_bwd - gradients of csa_sparse_mla_fwd ([HP] 4.
+ * npu_sparse_flash_mla_grad: the operator's backward returns d_query, d_ori_kv,
+ * d_cmp_kv, d_sinks and the window / compressed "softmax_l1_norm").
+ *
+ * Same key sets, softmax and sink as the forward, K = V.  With the forward's out and
+ * lse and the output gradient dout, for each query i and head h:
+ *   P[h,k] = exp(scale <q,kv_k> - lse),  dP[h,k] = <dout, kv_k>,  D = <dout, out>,
+ *   dS = P (dP - D),  dq = scale sum_k dS kv_k,
+ *   d_kv[row of k] += sum_h (scale dS q + P dout)   (window rows into d_ori_kv,
+ *                                                    compressed rows into d_cmp_kv),
+ *   d_sinks[h] = -sum_i exp(sinks[h] - lse) D.
+ * ori_l1[i, k] (window slot k = stream row lo + k, the csa_build_indices win_idx
+ * order) and cmp_l1[i, j] (the j-th attended compressed row: the j-th valid entry of
+ * the cmp_idx row, or visible row q_cmp_lo + j in attend-all mode) hold P averaged
+ * over the heads; unused slots are 0.  P and scale * dS enter the MFMA products as
+ * bf16, all accumulation is float32.
+ *   q, out, dout, dq [Tq, H, d] (call dtype), lse [Tq, H] float32 (the forward's),
+ *   d_ori_kv [Tkv, d] and d_cmp_kv [Tc, d] float32 (overwritten; Tc = rows of
+ *   cmp_kv), d_sinks [H] float32 (overwritten when sinks is given),
+ *   ori_l1 [Tq, W] float32, cmp_l1 [Tq, cmp_slots] float32 (optional, overwritten),
+ *   W = ori_win_left + ori_win_right + 1.
+ * max_seqlen_kv bounds the longest segment (attend-all mode sizes its key list from
+ * it).  workspace: device memory of at least csa_sparse_mla_bwd_workspace_bytes()
+ * bytes (P and dS fragments of every tile, key rows, sink terms), owned by the
+ * caller; no memory is allocated.
+ * Errors: as csa_sparse_mla_fwd, plus EINVAL for a missing out/lse/dout/dq/
+ * workspace/d_ori_kv, cmp_kv without d_cmp_kv, sinks without d_sinks, cmp_l1 with
+ * cmp_slots < 1, or a workspace smaller than required; EUNSUPPORTED for any shape
+ * other than (H, d) = (64, 512) bf16.
+ */
+int64_t csa_sparse_mla_bwd_workspace_bytes(int32_t Tq, int32_t ori_win_left, int32_t ori_win_right,
+                                           const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
+                                           int32_t max_seqlen_kv, int32_t cmp_ratio);
+int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
+                       int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d, int32_t dtype,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp,
+                       int32_t B, int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left,
+                       int32_t ori_win_right, int32_t max_seqlen_kv, const float* sinks, float softmax_scale,
+                       const void* out, const float* lse, const void* dout, void* dq, float* d_ori_kv,
+                       float* d_cmp_kv, float* d_sinks, float* ori_l1, float* cmp_l1, int32_t cmp_slots,
+                       void* workspace, int64_t workspace_bytes, csa_stream_t stream);
+
+/*
  * csa_validate_layout - synchronous debug check of a THD layout held in device
  * memory: cu_seqlens_kv starts at 0, is non-decreasing and ends at Tkv;
  * cu_seqlens_q equals clamp(cu_seqlens_kv - global_start, 0, Tq); and the longest

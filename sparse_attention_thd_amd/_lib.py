@@ -30,8 +30,12 @@ SIGNATURES = {
     "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
     "csa_sparse_mla_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P,
                            C.c_float, _P, _P, _P],
+    "csa_sparse_mla_bwd_workspace_bytes": [_I, _I, _I, _P, _P, _I, _I, _I],
+    "csa_sparse_mla_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
+                           C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, C.c_int64, _P],
     "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _P],
 }
+RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64}
 
 
 class CsaError(RuntimeError):
@@ -47,7 +51,7 @@ def _load() -> C.CDLL:
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
-        fn.restype = C.c_char_p if name in ("csa_version", "csa_last_error") else C.c_int
+        fn.restype = RESTYPES.get(name, C.c_int)
     return lib
 
 
@@ -140,6 +144,35 @@ def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, H, d, cu_seqle
         _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True), B, global_start, cmp_ratio, ori_win_left,
         ori_win_right, _ptr(sinks, "sinks", torch.float32, True), float(softmax_scale), _ptr(out, "out", dt),
         _ptr(lse, "lse", torch.float32, True), _stream(stream)))
+
+
+def csa_sparse_mla_bwd_workspace_bytes(Tq, ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv,
+                                       cmp_ratio):
+    n = LIB.csa_sparse_mla_bwd_workspace_bytes(Tq, ori_win_left, ori_win_right, _ptr(cmp_kv, "cmp_kv", optional=True),
+                                               _ptr(cmp_idx, "cmp_idx", torch.int32, True), topk, max_seqlen_kv,
+                                               cmp_ratio)
+    if n < 0:
+        raise CsaError(CSA_EINVAL, "csa_sparse_mla_bwd_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def csa_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv,
+                       cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv,
+                       sinks, softmax_scale, out, lse, dout, dq, d_ori_kv, d_cmp_kv=None, d_sinks=None,
+                       ori_l1=None, cmp_l1=None, cmp_slots=0, workspace=None, stream=None):
+    i32, f32 = torch.int32, torch.float32
+    dt = q.dtype
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.csa_sparse_mla_bwd(
+        _ptr(q, "q"), _ptr(ori_kv, "ori_kv", dt), _ptr(cmp_kv, "cmp_kv", dt, True),
+        _ptr(cmp_idx, "cmp_idx", i32, True), topk, Tq, Tkv, Tc, H, d, _dtype_code(q),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True), B, global_start, cmp_ratio, ori_win_left, ori_win_right,
+        max_seqlen_kv, _ptr(sinks, "sinks", f32, True), float(softmax_scale), _ptr(out, "out", dt),
+        _ptr(lse, "lse", f32), _ptr(dout, "dout", dt), _ptr(dq, "dq", dt), _ptr(d_ori_kv, "d_ori_kv", f32),
+        _ptr(d_cmp_kv, "d_cmp_kv", f32, True), _ptr(d_sinks, "d_sinks", f32, True), _ptr(ori_l1, "ori_l1", f32, True),
+        _ptr(cmp_l1, "cmp_l1", f32, True), cmp_slots, _ptr(workspace, "workspace", optional=True), ws_bytes,
+        _stream(stream)))
 
 
 def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, stream=None):

@@ -134,6 +134,66 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
                     "csa_sparse_mla_fwd");
 }
 
+// Keys per query the backward may see: the window (no longer than a segment) plus the
+// selected rows, or every visible compressed row (at most max_seqlen_kv / cmp_ratio)
+// in attend-all mode.
+static int bwd_key_cap(int32_t wl, int32_t wr, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
+                       int32_t max_seqlen_kv, int32_t cmp_ratio) {
+  long long W = static_cast<long long>(wl) + wr + 1;
+  if (W > max_seqlen_kv) W = max_seqlen_kv > 0 ? max_seqlen_kv : 1;
+  long long c = 0;
+  if (cmp_kv) c = cmp_idx ? topk : max_seqlen_kv / cmp_ratio;
+  return static_cast<int>(W + c > (1LL << 30) ? (1LL << 30) : W + c);
+}
+
+int64_t csa_sparse_mla_bwd_workspace_bytes(int32_t Tq, int32_t ori_win_left, int32_t ori_win_right,
+                                           const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
+                                           int32_t max_seqlen_kv, int32_t cmp_ratio) {
+  if (Tq < 0 || ori_win_left < 0 || ori_win_right < 0 || cmp_ratio < 1 || max_seqlen_kv < 0) return -1;
+  const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
+  return static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap));
+}
+
+int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
+                       int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d, int32_t dtype,
+                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp,
+                       int32_t B, int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left,
+                       int32_t ori_win_right, int32_t max_seqlen_kv, const float* sinks, float softmax_scale,
+                       const void* out, const float* lse, const void* dout, void* dq, float* d_ori_kv,
+                       float* d_cmp_kv, float* d_sinks, float* ori_l1, float* cmp_l1, int32_t cmp_slots,
+                       void* workspace, int64_t workspace_bytes, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv || !ori_kv || !d_ori_kv ||
+      (Tq != 0 && (!q || !out || !lse || !dout || !dq || !workspace)))
+    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: NULL pointer");
+  if (cmp_kv && (!cu_seqlens_cmp || !d_cmp_kv)) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: cmp_kv needs cu_seqlens_cmp and d_cmp_kv");
+  if (cmp_idx && !cmp_kv) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: cmp_idx given without cmp_kv");
+  if (cmp_idx && topk < 1) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: topk must be >= 1 with cmp_idx");
+  if (sinks && !d_sinks) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: sinks need d_sinks");
+  if (cmp_l1 && cmp_slots < 1) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: cmp_l1 needs cmp_slots >= 1");
+  if (B < 1 || Tq < 0 || Tkv < 0 || Tc < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0 ||
+      max_seqlen_kv < 0 || cmp_slots < 0)
+    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: invalid size or parameter");
+  if (ori_win_left < 0 || ori_win_right < 0) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: window sides must be >= 0");
+  if (static_cast<long long>(global_start) + Tq > Tkv)
+    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: global_start + Tq exceeds Tkv");
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: unknown dtype %d", dtype);
+  if (cmp_idx && topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_bwd: topk %d > %d", topk, kMaxTopk);
+  if (!csa::mla_bwd_shape_supported(H, d, dtype))
+    return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_bwd: no kernel for H=%d d=%d dtype=%d", H, d, dtype);
+  const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
+  const int64_t need = static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap));
+  if (workspace_bytes < need)
+    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: workspace of %lld bytes < %lld needed",
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+  return hip_status(csa::launch_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, cmp_kv ? Tc : 0,
+                                               cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
+                                               cmp_ratio, ori_win_left, ori_win_right, sinks, softmax_scale, out,
+                                               lse, dout, dq, d_ori_kv, cmp_kv ? d_cmp_kv : nullptr, d_sinks, ori_l1,
+                                               cmp_l1, cmp_slots, cap, workspace,
+                                               static_cast<hipStream_t>(stream)),
+                    "csa_sparse_mla_bwd");
+}
+
 int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B, int32_t Tq,
                         int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv, csa_stream_t stream) {
   if (!cu_seqlens_q || !cu_seqlens_kv || B < 1 || Tq < 0 || Tkv < 0 || global_start < 0)

@@ -108,6 +108,38 @@ def test_sparse_mla_rejects(kw, code):
     assert _mla(**kw) == code
 
 
+def _mla_bwd(**kw):
+    a = dict(q=FAKE, kv=FAKE, ckv=FAKE, cidx=FAKE, topk=512, Tq=8, Tkv=8, Tc=2, H=64, d=512, dtype=1, cu_q=FAKE,
+             cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, wl=127, wr=0, maxlen=8, sinks=FAKE, scale=0.04, out=FAKE,
+             lse=FAKE, dout=FAKE, dq=FAKE, dkv=FAKE, dcmp=FAKE, dsinks=FAKE, ol1=None, cl1=None, slots=0,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return LIB.csa_sparse_mla_bwd(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), EINVAL), (dict(dout=None), EINVAL), (dict(lse=None), EINVAL), (dict(dq=None), EINVAL),
+    (dict(ws=None), EINVAL), (dict(dkv=None), EINVAL), (dict(dcmp=None), EINVAL), (dict(dsinks=None), EINVAL),
+    (dict(ckv=None), EINVAL), (dict(topk=0), EINVAL), (dict(cl1=FAKE, slots=0), EINVAL), (dict(B=0), EINVAL),
+    (dict(gs=1), EINVAL), (dict(wr=-1), EINVAL), (dict(ws_bytes=1024), EINVAL), (dict(topk=4096), EUNSUP),
+    (dict(H=16), EUNSUP), (dict(dtype=0), EUNSUP),
+])
+def test_sparse_mla_bwd_rejects(kw, code):
+    assert _mla_bwd(**kw) == code
+
+
+def test_sparse_mla_bwd_workspace_size_formula():
+    # per query: ceil(keys / 32) tiles x (8 KiB of P / dS fragments + 32 key rows x 4 B) + 4 B + 64 sink terms x 4 B
+    n = LIB.csa_sparse_mla_bwd_workspace_bytes(10, 127, 0, FAKE, FAKE, 512, 4096, 4)
+    assert n == 10 * (20 * (8192 + 128) + 4 + 256)
+    n_all = LIB.csa_sparse_mla_bwd_workspace_bytes(3, 127, 0, FAKE, None, 0, 1000, 4)  # attend-all: 128 + 250 keys
+    assert n_all == 3 * (12 * (8192 + 128) + 4 + 256)
+    assert LIB.csa_sparse_mla_bwd_workspace_bytes(-1, 127, 0, None, None, 0, 0, 4) == -1
+    # a window wider than the longest segment holds at most max_seqlen_kv keys
+    n_wide = LIB.csa_sparse_mla_bwd_workspace_bytes(2, 100000, 0, None, None, 0, 300, 4)
+    assert n_wide == 2 * (10 * (8192 + 128) + 4 + 256)
+
+
 def test_validate_layout_rejects_bad_arguments():
     assert LIB.csa_validate_layout(None, FAKE, 1, 0, 0, 0, -1, None) == EINVAL
     assert LIB.csa_validate_layout(FAKE, FAKE, 0, 0, 0, 0, -1, None) == EINVAL
