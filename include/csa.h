@@ -205,10 +205,16 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
  *   cmp_kv), d_sinks [H] float32 (overwritten when sinks is given),
  *   ori_l1 [Tq, W] float32, cmp_l1 [Tq, cmp_slots] float32 (optional, overwritten),
  *   W = ori_win_left + ori_win_right + 1.
- * max_seqlen_kv bounds the longest segment (attend-all mode sizes its key list from
- * it).  workspace: device memory of at least csa_sparse_mla_bwd_workspace_bytes()
- * bytes (P and dS fragments of every tile, key rows, sink terms), owned by the
- * caller; no memory is allocated.
+ * Precondition of the sparse mode: the valid entries of a cmp_idx row are distinct
+ * rows visible to the query ([q_cmp_lo, q_cmp_lo + q_cmp_nvis)), as csa_indexer_topk
+ * emits them; the row gradients of other entries are not formed.
+ * max_seqlen_kv bounds the longest segment (it sizes the attend-all key list, the
+ * selection map and the row-gradient work items).  workspace: device memory of at
+ * least csa_sparse_mla_bwd_workspace_bytes() bytes (scale*dS and P of every
+ * (query, key) pair as 256-byte rows, key rows, sink terms, the selection map),
+ * owned by the caller; no memory is allocated.  d_ori_kv and d_cmp_kv take float
+ * atomics from the work items that share a key tile, so their last bits vary from
+ * run to run; dq, d_sinks and the l1 outputs are deterministic.
  * Errors: as csa_sparse_mla_fwd, plus EINVAL for a missing out/lse/dout/dq/
  * workspace/d_ori_kv, cmp_kv without d_cmp_kv, sinks without d_sinks, cmp_l1 with
  * cmp_slots < 1, or a workspace smaller than required; EUNSUPPORTED for any shape

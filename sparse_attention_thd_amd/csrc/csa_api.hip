@@ -146,12 +146,18 @@ static int bwd_key_cap(int32_t wl, int32_t wr, const void* cmp_kv, const int32_t
   return static_cast<int>(W + c > (1LL << 30) ? (1LL << 30) : W + c);
 }
 
+// Visible compressed rows per query at most (the selection map of the sparse mode).
+static int bwd_nvis_cap(const void* cmp_kv, const int32_t* cmp_idx, int32_t max_seqlen_kv, int32_t cmp_ratio) {
+  return (cmp_kv && cmp_idx) ? max_seqlen_kv / cmp_ratio : 0;
+}
+
 int64_t csa_sparse_mla_bwd_workspace_bytes(int32_t Tq, int32_t ori_win_left, int32_t ori_win_right,
                                            const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
                                            int32_t max_seqlen_kv, int32_t cmp_ratio) {
   if (Tq < 0 || ori_win_left < 0 || ori_win_right < 0 || cmp_ratio < 1 || max_seqlen_kv < 0) return -1;
   const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
-  return static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap));
+  return static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap, bwd_nvis_cap(cmp_kv, cmp_idx, max_seqlen_kv,
+                                                                                 cmp_ratio)));
 }
 
 int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
@@ -181,15 +187,17 @@ int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, co
   if (!csa::mla_bwd_shape_supported(H, d, dtype))
     return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_bwd: no kernel for H=%d d=%d dtype=%d", H, d, dtype);
   const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
-  const int64_t need = static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap));
+  const int nvis_cap = bwd_nvis_cap(cmp_kv, cmp_idx, max_seqlen_kv, cmp_ratio);
+  const int64_t need = static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap, nvis_cap));
   if (workspace_bytes < need)
     return fail(CSA_EINVAL, "csa_sparse_mla_bwd: workspace of %lld bytes < %lld needed",
                 static_cast<long long>(workspace_bytes), static_cast<long long>(need));
   return hip_status(csa::launch_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, cmp_kv ? Tc : 0,
                                                cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
-                                               cmp_ratio, ori_win_left, ori_win_right, sinks, softmax_scale, out,
-                                               lse, dout, dq, d_ori_kv, cmp_kv ? d_cmp_kv : nullptr, d_sinks, ori_l1,
-                                               cmp_l1, cmp_slots, cap, workspace,
+                                               cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks,
+                                               softmax_scale, out, lse, dout, dq, d_ori_kv,
+                                               cmp_kv ? d_cmp_kv : nullptr, d_sinks, ori_l1, cmp_l1, cmp_slots, cap,
+                                               nvis_cap, workspace,
                                                static_cast<hipStream_t>(stream)),
                     "csa_sparse_mla_bwd");
 }

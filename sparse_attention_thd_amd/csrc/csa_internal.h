@@ -28,14 +28,14 @@ hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_
 hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
                                  int topk, int Tq, int Tkv, int Tc, const int32_t* cu_q, const int32_t* cu_kv,
                                  const int32_t* cu_cmp, int B, int global_start, int r, int wl, int wr,
-                                 const float* sinks, float scale, const void* out, const float* lse,
-                                 const void* dout, void* dq, float* d_ori, float* d_cmp, float* d_sinks,
-                                 float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap, void* workspace,
-                                 hipStream_t s);
+                                 int max_seqlen_kv, const float* sinks, float scale, const void* out,
+                                 const float* lse, const void* dout, void* dq, float* d_ori, float* d_cmp,
+                                 float* d_sinks, float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap,
+                                 int nvis_cap, void* workspace, hipStream_t s);
 
 bool indexer_shape_supported(int H_I, int d_I, int dtype);
 bool mla_shape_supported(int H, int d, int dtype);
 bool mla_bwd_shape_supported(int H, int d, int dtype);
-size_t mla_bwd_workspace_bytes(int Tq, int key_cap);
+size_t mla_bwd_workspace_bytes(int Tq, int key_cap, int nvis_cap);
 
 }  // namespace csa

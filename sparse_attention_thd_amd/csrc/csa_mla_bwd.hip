@@ -4,14 +4,20 @@
 //   P = exp(scale q.kv - lse),  dP = dout.kv,  D = dout.out,  dS = P (dP - D)
 //   dq = scale sum_k dS kv,   dkv[k] += sum_h (scale dS q + P dout),   dsink = -sum p_sink D
 //
-// Four kernels on the caller's stream, all one workgroup (4 wavefronts x 16 heads, or
-// x 128 latent dims) per query, sharing the forward's tile machinery:
-//   prep  S^T and dP^T tile by tile from one K fragment each (K = V), P and
-//         scale * dS as bf16 MFMA fragments into the workspace, the key row of every
-//         tile slot, the head-averaged probabilities and the per-query sink terms;
-//   dq    O^T-style accumulation dq^T += K^T (scale dS)^T from the same tiles;
-//   dkv   (dims x keys) = Q^T (scale dS)^T + dout^T P^T per tile, added to the float32
-//         row gradients with float atomics (a row is shared by many queries);
+// Kernels on the caller's stream:
+//   prep  query-major (one workgroup of 4 wavefronts x 16 heads per query): S and dP
+//         tile by tile from one kv fragment each (K = V) against the query's q and dout
+//         held in registers; writes scale * dS and P of every (query, key) pair as a
+//         256-byte slot row (64 heads each, bf16), the key row of every slot, the
+//         head-averaged probabilities and the per-query sink terms;
+//   dq    query-major: dq^T += kv^T (scale dS)^T per tile, kv and the dS rows staged in
+//         LDS;
+//   dkv   key-major: a workgroup owns 128 keys (window rows or compressed rows of one
+//         segment) x 256 latent dims and sweeps up to 128 queries, accumulating
+//         C[keys x dims] += [scale dS | P][keys x (head, term)] . [q ; dout] in
+//         registers (32x32x16 MFMAs), then adds C to the float32 row gradients.  Only
+//         the query chunks of one key tile meet in the atomics, so the row gradients
+//         take a few float atomics per element instead of one per (query, key) pair;
 //   sinks one reduction per head over the per-query sink terms.
 #include "csa_common.h"
 #include "csa_internal.h"
@@ -20,49 +26,73 @@
 namespace csa {
 namespace {
 
-constexpr int kFragBytes = kWaves * 64 * 16;  // one 16-byte fragment per lane of 4 wavefronts
-constexpr int kTileWs = 2 * kFragBytes;       // P and scale * dS fragments of one tile
+constexpr int kSlotBytes = 256;  // scale * dS (bytes 0..127) then P (128..255), 64 heads bf16 each
+constexpr int kGK = 128;         // keys per dkv tile
+constexpr int kQCH = 128;        // queries per dkv work item
+constexpr int kYRow = 512;       // staged q / dout half row: 256 dims
+constexpr int kYBytes = 128 * kYRow;  // 64 q rows then 64 dout rows of one query
+constexpr int kDsStride = 144;   // staged dS row of the dq pass (128 bytes + pad)
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct BwdWorkspace {
-  unsigned char* frags;  // [Tq][ntc][2][kFragBytes]
-  int32_t* rows;         // [Tq][ntc][32] key row codes: window row r >= 0, compressed row c -> -1 - c
-  int32_t* nkeys;        // [Tq]
+  unsigned char* slots;  // [Tq][nslot][kSlotBytes]
+  int32_t* codes;        // [Tq][nslot] key row of a slot: window row r >= 0, compressed row c -> -1 - c
   float* sink_terms;     // [Tq][64]
+  int32_t* nkeys;        // [Tq]
+  int16_t* cmap;         // [Tq][nvis_cap] compacted index of each visible compressed row, -1 if not selected
 };
 
-__host__ __device__ inline size_t ws_bytes(long long Tq, int ntc) {
-  return static_cast<size_t>(Tq) * (static_cast<size_t>(ntc) * (kTileWs + 32 * 4) + 4 + 64 * 4);
+__host__ __device__ inline size_t ws_bytes(long long Tq, int nslot, int nvis_cap) {
+  return static_cast<size_t>(Tq) *
+         (static_cast<size_t>(nslot) * (kSlotBytes + 4) + 64 * 4 + 4 + static_cast<size_t>(nvis_cap) * 2);
 }
 
-__host__ __device__ inline BwdWorkspace ws_layout(void* base, long long Tq, int ntc) {
+__host__ __device__ inline BwdWorkspace ws_layout(void* base, long long Tq, int nslot) {
   BwdWorkspace w;
   unsigned char* p = static_cast<unsigned char*>(base);
-  w.frags = p;
-  p += static_cast<size_t>(Tq) * ntc * kTileWs;
-  w.rows = reinterpret_cast<int32_t*>(p);
-  p += static_cast<size_t>(Tq) * ntc * 32 * 4;
+  w.slots = p;
+  p += static_cast<size_t>(Tq) * nslot * kSlotBytes;
+  w.codes = reinterpret_cast<int32_t*>(p);
+  p += static_cast<size_t>(Tq) * nslot * 4;
+  w.sink_terms = reinterpret_cast<float*>(p);
+  p += static_cast<size_t>(Tq) * 64 * 4;
   w.nkeys = reinterpret_cast<int32_t*>(p);
   p += static_cast<size_t>(Tq) * 4;
-  w.sink_terms = reinterpret_cast<float*>(p);
+  w.cmap = reinterpret_cast<int16_t*>(p);
   return w;
 }
 
-// Key ranges of query i (segment search by ballot; compressed count only in
-// attend-all mode, the selection mode fills it in from the compaction).
-__device__ QueryKeys bwd_ranges(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
-                                const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
-                                bool attend_all, int Tc) {
+struct BwdKeys {
+  int b, s, e;   // segment and its stream rows [s, e)
+  int lo, nwin;  // window rows lo .. lo + nwin - 1
+  int cmp_base;  // first compressed row of the segment
+  int nvis;      // causally complete compressed rows of the segment (below Tc)
+  int ncmp;      // attended compressed rows
+};
+
+// Key ranges of local query i (segment search by ballot).  Window sides are clamped
+// to Tkv by the launcher, so t + wr cannot overflow.
+__device__ BwdKeys bwd_ranges(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+                              const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
+                              bool attend_all, int Tc) {
   const int lane = threadIdx.x & 63;
   int count = 0;
   for (int base = 0; base < B; base += 64) count += __popcll(__ballot(base + lane < B && cu_q[base + lane] <= i));
-  const int b = __builtin_amdgcn_readfirstlane(count - 1);
+  BwdKeys k;
+  k.b = __builtin_amdgcn_readfirstlane(count - 1);
   const int t = global_start + i;
-  const int s = cu_kv[b], e = cu_kv[b + 1];
-  QueryKeys k;
-  k.lo = max(s, t - wl);
-  k.nwin = min(e - 1, t + wr) - k.lo + 1;
-  k.cmp_base = (cu_cmp != nullptr) ? cu_cmp[b] : 0;
-  k.ncmp = attend_all ? max(0, min((t - s + 1) / r, min(cu_cmp[b + 1], Tc) - k.cmp_base)) : 0;
+  k.s = cu_kv[k.b];
+  k.e = cu_kv[k.b + 1];
+  k.lo = max(k.s, t - wl);
+  k.nwin = min(k.e - 1, t + wr) - k.lo + 1;
+  k.cmp_base = 0;
+  k.nvis = 0;
+  if (cu_cmp != nullptr) {
+    k.cmp_base = cu_cmp[k.b];
+    k.nvis = max(0, min((t - k.s + 1) / r, min(cu_cmp[k.b + 1], Tc) - k.cmp_base));
+  }
+  k.ncmp = attend_all ? k.nvis : 0;
   return k;
 }
 
@@ -73,9 +103,9 @@ __global__ void zero_f32_kernel(float* __restrict__ p, long long n) {
     p[k] = 0.f;
 }
 
-// Q-style B operand of S^T = K . X^T (X = q or dout): k-slot 8g + j of MFMA step ks
+// Q-style MFMA operand of a head row (X = q, dout or out): k-slot 8g + j of MFMA step ks
 // stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 + 4*g + (j - 4), the
-// permutation the K fragments use.
+// permutation the kv fragments use.
 __device__ __forceinline__ void load_qstyle(const uint16_t* __restrict__ row, bf16x8 (&f)[16]) {
 #pragma unroll
   for (int ks = 0; ks < 16; ++ks) {
@@ -93,7 +123,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t* __restrict__ cmp_idx, int topk, int Tq, int Tc, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
     int wr, const float* __restrict__ sinks, float scale, const uint16_t* __restrict__ out,
-    const float* __restrict__ lse, const uint16_t* __restrict__ dout, void* ws_base, int ntc,
+    const float* __restrict__ lse, const uint16_t* __restrict__ dout, void* ws_base, int nslot, int nvis_cap,
     float* __restrict__ ori_l1, int W, float* __restrict__ cmp_l1, int cmp_slots) {
   __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
   __shared__ int32_t crow[kMaxTopk];
@@ -107,7 +137,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int n = lane & 15, g = lane >> 4;
   const int head = 16 * wave + n;
   const bool sparse = cmp_kv != nullptr && cmp_idx != nullptr;
-  const BwdWorkspace ws = ws_layout(ws_base, Tq, ntc);
+  const BwdWorkspace ws = ws_layout(ws_base, Tq, nslot);
   const float scale_log2 = scale * kLog2e;
 
   int vals[NC];
@@ -123,7 +153,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   bf16x8 qf[16], df[16];
   load_qstyle(q + qoff, qf);
   load_qstyle(dout + qoff, df);
-  // D = dout . out for this lane's head: each lane sums its 128 dims, then the quad
+  // D = dout . out of head 16 wave + n: each lane sums its 128 dims, then the quad
   float dsum = 0.f;
   {
     bf16x8 of[16];
@@ -134,17 +164,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int j = 0; j < 8; ++j) dsum += static_cast<float>(df[ks][j]) * static_cast<float>(of[ks][j]);
   }
   const float Dh = quad_sum(dsum);
-  const float lse2 = lse[static_cast<long long>(i) * 64 + head] * kLog2e;
+  const float lse2_h = lse[static_cast<long long>(i) * 64 + head] * kLog2e;
+  // The S tiles (heads x keys) give lane (n, g) the heads 16 wave + 4 g + j.
+  float lse2[4], Dq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lse2[j] = __shfl(lse2_h, 4 * g + j, 64);
+    Dq[j] = __shfl(Dh, 4 * g + j, 64);
+  }
 
+  BwdKeys qk = bwd_ranges(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr && !sparse, Tc);
   // compressed rows past the caller's Tc are never read (nor their gradients written)
-  QueryKeys qk = bwd_ranges(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr && !sparse, Tc);
   if (sparse) qk.ncmp = compact_rows(vals, topk, min(cu_cmp[B], Tc), crow, wsum);
-  // the workspace holds at most ntc tiles per query
-  const int nkeys = min(qk.nwin + qk.ncmp, ntc * kNT);
+  const int nkeys = min(qk.nwin + qk.ncmp, nslot);  // the workspace holds nslot keys per query
   const int ntiles = (nkeys + kNT - 1) / kNT;
   if (tid == 0) ws.nkeys[i] = nkeys;
   if (sinks != nullptr && g == 0)
-    ws.sink_terms[static_cast<long long>(i) * 64 + head] = -exp2f(sinks[head] * kLog2e - lse2) * Dh;
+    ws.sink_terms[static_cast<long long>(i) * 64 + head] = -exp2f(sinks[head] * kLog2e - lse2_h) * Dh;
+  // Map of the visible compressed rows for the key-major dkv pass (sparse mode): the
+  // compacted index of each selected row, -1 elsewhere.
+  if (sparse && nvis_cap > 0) {
+    int16_t* m = ws.cmap + static_cast<long long>(i) * nvis_cap;
+    const int nv = min(qk.nvis, nvis_cap);
+    for (int v = tid; v < nv; v += kThreads) m[v] = -1;
+    __syncthreads();  // the -1 fill lands before the entries below
+    for (int j = tid; j < qk.ncmp; j += kThreads) {
+      const int v = crow[j] - qk.cmp_base;
+      if (v >= 0 && v < nv && qk.nwin + j < nslot) m[v] = static_cast<int16_t>(j);
+    }
+  }
   const bool want_l1 = ori_l1 != nullptr || cmp_l1 != nullptr;
 
   const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
@@ -172,9 +220,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                  kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
     }
   };
-  // key rows of every tile slot, for the dq and dkv passes (slots past nkeys: code of key 0)
+  // key rows of every slot, for the dq pass (slots past nkeys: the row of key 0)
   for (int k = tid; k < ntiles * kNT; k += kThreads)
-    ws.rows[static_cast<long long>(i) * ntc * kNT + k] = key_code(k < nkeys ? k : 0);
+    ws.codes[static_cast<long long>(i) * nslot + k] = key_code(k < nkeys ? k : 0);
   if (ntiles > 0) issue(0, 0);
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
@@ -193,61 +241,59 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
   };
+  unsigned char* slot_base = ws.slots + static_cast<long long>(i) * nslot * kSlotBytes + 2 * (16 * wave + 4 * g);
 
   for (int t = 0; t < ntiles; ++t) {
     const int bf = t & 1;
-    // this wavefront's rows of tile t have landed and its LDS adds of tile t - 1 are done
+    // this wavefront's rows of tile t have landed and its LDS writes of tile t - 1 are done
     __builtin_amdgcn_s_waitcnt(0x0070);
     tile_barrier();  // all rows landed; buffer bf ^ 1 is free; l1s[bf ^ 1] is complete
     if (t + 1 < ntiles) issue(t + 1, bf ^ 1);
     if (want_l1 && t > 0) flush_l1(t - 1);
     const unsigned char* tb = kt + bf * kTileBytes;
 
-    // ---- S^T = K . Q^T and dP^T = K . dout^T from the same K fragments (K = V)
+    // ---- S = Q . K^T and dP = dout . K^T (heads x keys) from the same K fragments (K = V)
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
       const bf16x8 a0 = kfrag(tb, offq + 64 * ks, offq + 64 * ks + 32);
       const bf16x8 a1 = kfrag(tb + 16 * kRowStride, offq + 64 * ks, offq + 64 * ks + 32);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qf[ks], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qf[ks], s1, 0, 0, 0);
-      p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, df[ks], p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, df[ks], p1, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], a0, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], a1, s1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], a0, p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], a1, p1, 0, 0, 0);
     }
 
-    // ---- P and scale * dS for keys kpi(4g+j) (j < 4) and 16 + kpi(4g+j-4); masked keys 0
-    bf16x8 pf, sf;
-    float pv[8];
+    // ---- lane (n, g): keys kpi(n) and 16 + kpi(n) of the tile, heads 16 wave + 4 g + j
+    const int k0 = kpi(n), k1 = 16 + kpi(n);
+    const bool v0 = t * kNT + k0 < nkeys, v1 = t * kNT + k1 < nkeys;
+    bf16x4 P0, P1, S0, S1;
+    float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int kk = (j < 4) ? kpi(4 * g + j) : 16 + kpi(4 * g + j - 4);
-      const float sv = (j < 4) ? s0[j] : s1[j - 4];
-      const float dp = (j < 4) ? p0[j] : p1[j - 4];
-      const float p = (t * kNT + kk < nkeys) ? exp2f(sv * scale_log2 - lse2) : 0.f;
-      pv[j] = p;
-      pf[j] = static_cast<__bf16>(p);
-      sf[j] = static_cast<__bf16>(scale * p * (dp - Dh));
+    for (int j = 0; j < 4; ++j) {
+      const float pa = v0 ? exp2f(s0[j] * scale_log2 - lse2[j]) : 0.f;
+      const float pb = v1 ? exp2f(s1[j] * scale_log2 - lse2[j]) : 0.f;
+      P0[j] = static_cast<__bf16>(pa);
+      P1[j] = static_cast<__bf16>(pb);
+      S0[j] = static_cast<__bf16>(scale * pa * (p0[j] - Dq[j]));
+      S1[j] = static_cast<__bf16>(scale * pb * (p1[j] - Dq[j]));
+      l0 += pa;
+      l1 += pb;
     }
-    {
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      unsigned char* fb = ws.frags + (static_cast<long long>(i) * ntc + t) * kTileWs + wave * 1024 + lane * 16;
-      *reinterpret_cast<u32x4*>(fb) = __builtin_bit_cast(u32x4, pf);
-      *reinterpret_cast<u32x4*>(fb + kFragBytes) = __builtin_bit_cast(u32x4, sf);
-    }
+    unsigned char* row0 = slot_base + static_cast<long long>(t * kNT + k0) * kSlotBytes;
+    unsigned char* row1 = slot_base + static_cast<long long>(t * kNT + k1) * kSlotBytes;
+    *reinterpret_cast<uint2*>(row0) = __builtin_bit_cast(uint2, S0);
+    *reinterpret_cast<uint2*>(row0 + 128) = __builtin_bit_cast(uint2, P0);
+    *reinterpret_cast<uint2*>(row1) = __builtin_bit_cast(uint2, S1);
+    *reinterpret_cast<uint2*>(row1 + 128) = __builtin_bit_cast(uint2, P1);
     if (want_l1) {
-      // sum over the 16 heads of this wavefront (lanes n of one lane group); the
+      // sum over the 16 heads of this wavefront (4 per lane, then the lane quad); the
       // four wavefront sums meet in LDS
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float v = pv[j];
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 4, 64);
-        v += __shfl_xor(v, 8, 64);
-        if (n == 0) {
-          const int kk = (j < 4) ? kpi(4 * g + j) : 16 + kpi(4 * g + j - 4);
-          l1s[bf][wave][kk] = v;
-        }
+      l0 = quad_sum(l0);
+      l1 = quad_sum(l1);
+      if (g == 0) {
+        l1s[bf][wave][k0] = l0;
+        l1s[bf][wave][k1] = l1;
       }
     }
   }
@@ -260,22 +306,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ----------------------------------------------------------------------------- dq
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_dq_kernel(
-    const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv, int Tq, const void* ws_base, int ntc,
+    const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv, int Tq, const void* ws_base, int nslot,
     uint16_t* __restrict__ dq) {
   __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char dsb[2][kNT * kDsStride];
   const int i = static_cast<int>(blockIdx.x);
   if (i >= Tq) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, ntc);
+  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot);
   const int nkeys = __builtin_amdgcn_readfirstlane(ws.nkeys[i]);
   const int ntiles = (nkeys + kNT - 1) / kNT;
-  const int32_t* rows = ws.rows + static_cast<long long>(i) * ntc * kNT;
+  const int32_t* codes = ws.codes + static_cast<long long>(i) * nslot;
   const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
   const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
   auto issue = [&](int t, int bf) {
-    const int code = rows[t * kNT + 4 * (lane & 7) + wave];
+    const int code = codes[t * kNT + 4 * (lane & 7) + wave];
     const uint16_t* src = (code >= 0) ? ori_kv + static_cast<long long>(code) * 512
                                       : cmp_kv + static_cast<long long>(-1 - code) * 512;
     const unsigned long long a = reinterpret_cast<unsigned long long>(src);
@@ -289,29 +336,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                  kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
     }
   };
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  auto frag = [&](int t) {  // scale * dS^T fragment of tile t for this lane
-    const unsigned char* fb =
-        ws.frags + (static_cast<long long>(i) * ntc + t) * kTileWs + kFragBytes + wave * 1024 + lane * 16;
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(fb));
-  };
-  if (ntiles > 0) issue(0, 0);
-  bf16x8 sf = (ntiles > 0) ? frag(0) : bf16x8{};
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // this thread's 16 bytes of a tile's scale * dS rows: slot tid / 8, heads 8 (tid % 8) ..
+  const unsigned char* ds_src =
+      ws.slots + (static_cast<long long>(i) * nslot + (tid >> 3)) * kSlotBytes + (tid & 7) * 16;
+  const int ds_dst = (tid >> 3) * kDsStride + (tid & 7) * 16;
+  u32x4 dreg = {0u, 0u, 0u, 0u};
+  if (ntiles > 0) {
+    issue(0, 0);
+    dreg = *reinterpret_cast<const u32x4*>(ds_src);
+  }
   f32x4 o[32];
 #pragma unroll
   for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int offv = kpi(4 * g + (n >> 2)) * kRowStride + 8 * (n & 3);
+  // B operand (scale dS)^T through transpose reads: source lane m of lane group g points
+  // at slot kpi(4 g + m / 4), heads 16 wave + 4 (m % 4) .., so lane (n, g) receives head
+  // 16 wave + n at keys kpi(4 g + j) (and 16 + kpi(4 g + j) from the second read).
+  const int dso = kpi(4 * g + (n >> 2)) * kDsStride + 2 * (16 * wave + 4 * (n & 3));
   for (int t = 0; t < ntiles; ++t) {
     const int bf = t & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    tile_barrier();
-    bf16x8 sf_next = sf;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // kv rows of tile t landed (dreg is waited for by the compiler)
+    *reinterpret_cast<u32x4*>(dsb[bf] + ds_dst) = dreg;
+    lds_barrier();  // dS rows of tile t visible; every wavefront is done with tile t - 1
     if (t + 1 < ntiles) {
       issue(t + 1, bf ^ 1);
-      sf_next = frag(t + 1);
+      dreg = *reinterpret_cast<const u32x4*>(ds_src + static_cast<long long>(t + 1) * kNT * kSlotBytes);
     }
     const unsigned char* tb = kt + bf * kTileBytes;
+    const bf16x4 slo = ds_read_tr(dsb[bf] + dso);
+    const bf16x4 shi = ds_read_tr(dsb[bf] + dso + 16 * kDsStride);
+    const bf16x8 sf = {slo[0], slo[1], slo[2], slo[3], shi[0], shi[1], shi[2], shi[3]};
     bf16x4 vlo[4], vhi[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -330,7 +384,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    sf = sf_next;
   }
   // dq^T column (head 16w + n), dims 16 mb + 4 g + j; rows of 8 bytes per lane
   uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * wave + n) * 512 + 4 * g;
@@ -346,130 +399,284 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // ----------------------------------------------------------------------------- dkv
 
-// Per query, per tile: C[keys x dims] = (scale dS)[keys x heads] . q[heads x dims]
-// + P[keys x heads] . dout[heads x dims], wavefront w owning dims [128w, 128w+128).
-// MFMA k-slots run over heads: k-slot 8g + j of a 32-head half hh stands for head
-// 32 hh + 4 g + j (j < 4) or 32 hh + 16 + 4 g + (j - 4).  The q / dout B operands come
-// from transpose reads of the query's rows staged once in LDS; the dS / P A operands
-// from the tile's fragments regrouped through LDS as [key][head].
-constexpr int kQStride = 1040;  // staged q / dout rows (64 heads), padded like the tiles
-constexpr int kKH = 64 * 2 + 16; // staged [key][head] bf16 row, padded
+// Work items, per segment: window tiles (128 key rows) x query chunks of the tile's band,
+// then compressed tiles (128 compressed rows) x query chunks of the segment.  The counts
+// depend only on cu_seqlens, so every workgroup derives the item list itself.
+struct SegItems {
+  int nw, chunks_w, tiles_c, chunks_c;
+};
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_dkv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, int Tq, const void* ws_base, int ntc,
+__device__ __forceinline__ SegItems seg_items(int b, int B, const int32_t* __restrict__ cu_q,
+                                              const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
+                                              int wl, int wr, int Tc) {
+  SegItems it = {0, 0, 0, 0};
+  if (b >= B) return it;
+  const int L = cu_kv[b + 1] - cu_kv[b];
+  const int Lq = cu_q[b + 1] - cu_q[b];
+  if (L <= 0 || Lq <= 0) return it;
+  const long long band = static_cast<long long>(kGK) + wl + wr;
+  it.chunks_w = static_cast<int>((min(band, static_cast<long long>(Lq)) + kQCH - 1) / kQCH);
+  it.nw = (L + kGK - 1) / kGK * it.chunks_w;
+  if (cu_cmp != nullptr) {
+    const int Lc = max(0, min(cu_cmp[b + 1], Tc) - cu_cmp[b]);
+    it.tiles_c = (Lc + kGK - 1) / kGK;
+    it.chunks_c = (Lq + kQCH - 1) / kQCH;
+  }
+  return it;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(x, o, 64);
+    if (lane >= o) x += v;
+  }
+  return x;
+}
+
+// Staged q / dout rows: row r (q head r, or dout head r - 64), 16-byte chunk c of the
+// 256-dim half lives at chunk c ^ (4 (r % 4)), so that the transpose reads of one
+// half-wavefront (4 rows x 4 chunks) touch every bank once.
+__device__ __forceinline__ int ychunk(int row, int c) { return c ^ (4 * (row & 3)); }
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_bwd_dkv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, int Tq, const void* ws_base, int nslot,
+    int nvis_cap, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
+    const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr, int Tc, int sparse,
     float* __restrict__ d_ori, float* __restrict__ d_cmp) {
-  __shared__ __attribute__((aligned(1024))) unsigned char qs[64 * kQStride];
-  __shared__ __attribute__((aligned(16))) unsigned char kh[2][kNT * kKH];  // [P, scale dS][key][head]
-  const int i = static_cast<int>(blockIdx.x);
-  if (i >= Tq) return;
+  __shared__ __attribute__((aligned(1024))) unsigned char ybuf[2 * kYBytes];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, ntc);
-  const int nkeys = __builtin_amdgcn_readfirstlane(ws.nkeys[i]);
-  const int ntiles = (nkeys + kNT - 1) / kNT;
-  if (ntiles == 0) return;
-  const int32_t* rows = ws.rows + static_cast<long long>(i) * ntc * kNT;
+  const int wa = wave >> 1, wb = wave & 1;  // key half and dims half of the workgroup tile
+  const int half = static_cast<int>(blockIdx.y);
 
-  // B operands, constant per query: for dim block db (dims 128w + 16db ..) and head
-  // half hh, lane (n, g) holds X[heads of k-slots 8g..8g+7][dim 128w + 16db + n].
-  bf16x8 qb[8][2], db_[8][2];
-  auto stage_rows = [&](const uint16_t* __restrict__ src) {
-    // 64 head rows of 1 KiB: thread tid copies 16-byte chunks
-    for (int k = tid; k < 64 * 64; k += kThreads) {
-      const int h = k >> 6, c = k & 63;
-      *reinterpret_cast<uint4*>(qs + h * kQStride + c * 16) =
-          *reinterpret_cast<const uint4*>(src + (static_cast<long long>(i) * 64 + h) * 512 + c * 8);
+  // ---- the work item of this workgroup; consecutive items go to one XCD (the hardware
+  // deals workgroups to the 8 XCDs round robin), so neighbouring tiles share q / dout in L2
+  int total = 0;
+  for (int base = 0; base < B; base += 64) {
+    const SegItems it = seg_items(base + lane, B, cu_q, cu_kv, cu_cmp, wl, wr, Tc);
+    int c = it.nw + it.tiles_c * it.chunks_c;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
+    total += c;
+  }
+  total = __builtin_amdgcn_readfirstlane(total);
+  const int per = (total + 7) / 8;
+  const int x = static_cast<int>(blockIdx.x);
+  if (x / 8 >= per) return;
+  const int item = (x % 8) * per + x / 8;
+  if (item >= total) return;
+  int seg = -1, u = 0, run = 0;
+  for (int base = 0; base < B && seg < 0; base += 64) {
+    const SegItems it = seg_items(base + lane, B, cu_q, cu_kv, cu_cmp, wl, wr, Tc);
+    const int c = it.nw + it.tiles_c * it.chunks_c;
+    const int incl = wave_incl_scan(c) + run;
+    const unsigned long long hit = __ballot(incl - c <= item && item < incl && c > 0);
+    if (hit != 0ull) {
+      const int src = __builtin_ctzll(hit);
+      seg = base + src;
+      u = item - __shfl(incl - c, src, 64);
+    }
+    run = __shfl(incl, 63, 64);
+  }
+  seg = __builtin_amdgcn_readfirstlane(seg);
+  u = __builtin_amdgcn_readfirstlane(u);
+  if (seg < 0) return;
+  const SegItems it = seg_items(seg, B, cu_q, cu_kv, cu_cmp, wl, wr, Tc);
+  const int s = cu_kv[seg], e = cu_kv[seg + 1];
+  const int qa = cu_q[seg], qb = cu_q[seg + 1];
+  const bool win = u < it.nw;
+  int key0, key_end, i0, i1, cb = 0, nvis_seg = 0;
+  if (win) {
+    const int tile = u / it.chunks_w, chunk = u % it.chunks_w;
+    key0 = s + kGK * tile;
+    key_end = min(key0 + kGK, e);
+    const int band_lo = max(key0 - wr, global_start + qa);
+    const int band_hi = min(key_end - 1 + wl, global_start + qb - 1);
+    i0 = band_lo - global_start + chunk * kQCH;
+    i1 = min(band_hi - global_start + 1, i0 + kQCH);
+  } else {
+    const int v = u - it.nw;
+    const int chunk = v / it.tiles_c, tile = v % it.tiles_c;
+    cb = cu_cmp[seg];
+    nvis_seg = min(cu_cmp[seg + 1], Tc) - cb;
+    key0 = cb + kGK * tile;
+    key_end = min(key0 + kGK, cb + nvis_seg);
+    i0 = qa + chunk * kQCH;
+    i1 = min(qb, i0 + kQCH);
+    // the first query that sees row key0 sits at segment position (key0 - cb + 1) r - 1
+    const long long first = static_cast<long long>(s) + static_cast<long long>(key0 - cb + 1) * r - 1 - global_start;
+    if (first > i0) i0 = static_cast<int>(min(first, static_cast<long long>(i1)));
+  }
+  if (i0 >= i1) return;
+
+  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot);
+  const uint32_t yb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(ybuf)));
+
+  // ---- staging of query i's q and dout (this dims half) into ybuf[bf]: 64 wave
+  // instructions of 1 KiB (two rows each); wavefronts 0, 1 take q, 2, 3 take dout
+  auto stage = [&](int i, int bf) {
+    const uint16_t* src = (wave < 2 ? q : dout) + static_cast<long long>(i) * 64 * 512;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int uu = 16 * wave + v;
+      const int row = 2 * uu + (lane >> 5);
+      const uint32_t off = static_cast<uint32_t>((row & 63) * 1024 + half * 512 + ychunk(row, lane & 31) * 16);
+      row_to_lds(src, off, yb + static_cast<uint32_t>(bf * kYBytes + uu * 1024));
     }
   };
-  auto read_b = [&](bf16x8 (&b)[8][2]) {
-    const int rlo = 4 * g + (n >> 2);
-    const int coff = 2 * (128 * wave) + 8 * (n & 3);
-#pragma unroll
-    for (int d8 = 0; d8 < 8; ++d8)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const unsigned char* p = qs + (32 * hh + rlo) * kQStride + coff + 32 * d8;
-        const bf16x4 lo = ds_read_tr(p);
-        const bf16x4 hi = ds_read_tr(p + 16 * kQStride);
-        b[d8][hh] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+  // ---- A operand (keys x (term, head)) of query i: lane l holds key 32 kb + l % 32 of
+  // this wavefront's 64, k-slots 8 (l / 32) .. of step st = 4 term + head block.  Three
+  // steps, pipelined one query apart: the per-query inputs (slot count, selection-map
+  // entries), the slots, the slot rows.
+  struct Raw {
+    int nk;      // keys of the query in the workspace
+    int map[2];  // selection-map entry of this lane's key per key block (sparse compressed items)
   };
-  stage_rows(q);
-  __syncthreads();
-  read_b(qb);
-  __syncthreads();
-  stage_rows(dout);
-  __syncthreads();
-  read_b(db_);
-
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  for (int t = 0; t < ntiles; ++t) {
-    // regroup the tile's P and scale * dS fragments as [key][head]: wavefront w takes the
-    // fragments of head block w (lane (n, g): head 16w + n, keys kpi(4g+j), 16 + kpi(4g+j))
-    __syncthreads();  // previous tile's reads of kh are done
-    {
-      const unsigned char* fb = ws.frags + (static_cast<long long>(i) * ntc + t) * kTileWs + wave * 1024 + lane * 16;
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(fb));
-      const bf16x8 sf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(fb + kFragBytes));
-      const int h = 16 * wave + n;
+  auto load_raw = [&](int i) {
+    Raw w;
+    w.nk = ws.nkeys[i];
+    w.map[0] = w.map[1] = -1;
+    if (!win && sparse) {
+      const int t = global_start + i;
+      const int vis = min(min((t - s + 1) / r, nvis_seg), nvis_cap);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = (j < 4) ? kpi(4 * g + j) : 16 + kpi(4 * g + j - 4);
-        *reinterpret_cast<__bf16*>(kh[0] + kk * kKH + 2 * h) = pf[j];
-        *reinterpret_cast<__bf16*>(kh[1] + kk * kKH + 2 * h) = sf[j];
+      for (int kb = 0; kb < 2; ++kb) {
+        const int v = key0 + 64 * wa + 32 * kb + (lane & 31) - cb;
+        if (v < vis) w.map[kb] = ws.cmap[static_cast<long long>(i) * nvis_cap + v];
       }
     }
-    __syncthreads();
-    int code[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) code[kb][j] = rows[t * kNT + 16 * kb + 4 * g + j];
+    return w;
+  };
+  auto load_rows = [&](int i, const Raw& w, bf16x8 (&a)[2][8], bool (&act)[2]) {
+    const int t = global_start + i;
+    const int lo = max(s, t - wl);
+    const int nwin = min(e - 1, t + wr) - lo + 1;
+    const int vis = win ? 0 : min((t - s + 1) / r, nvis_seg);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      // A operands: key 16 kb + n, heads of the k-slot order, two 8-byte reads each
-      bf16x8 ap[2], as[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int o_lo = (16 * kb + n) * kKH + 2 * (32 * hh + 4 * g);
-        const int o_hi = o_lo + 2 * 16;
-        ap[hh] = kfrag(kh[0], o_lo, o_hi);
-        as[hh] = kfrag(kh[1], o_lo, o_hi);
-      }
-#pragma unroll
-      for (int d8 = 0; d8 < 8; ++d8) {
-        f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as[hh], qb[d8][hh], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ap[hh], db_[d8][hh], c, 0, 0, 0);
+      const int key = key0 + 64 * wa + 32 * kb + (lane & 31);
+      int slot = -1;
+      if (key < key_end) {
+        if (win) {
+          slot = key - lo;
+          if (slot >= nwin) slot = -1;
+        } else if (key - cb < vis) {
+          const int j = sparse ? w.map[kb] : key - cb;
+          slot = (j >= 0) ? nwin + j : -1;
         }
-        // C layout: lane (n, g) holds keys 16 kb + 4 g + j, dim 128w + 16 d8 + n
-        const int dim = 128 * wave + 16 * d8 + n;
+        if (slot >= w.nk) slot = -1;
+      }
+      act[kb] = __ballot(slot >= 0) != 0ull;
+      const unsigned char* p =
+          ws.slots + (static_cast<long long>(i) * nslot + max(slot, 0)) * kSlotBytes + 16 * (lane >> 5);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (t * kNT + 16 * kb + 4 * g + j >= nkeys) continue;
-          const int cd = code[kb][j];
-          float* dst = (cd >= 0) ? d_ori + static_cast<long long>(cd) * 512 + dim
-                                 : d_cmp + static_cast<long long>(-1 - cd) * 512 + dim;
-          atomicAdd(dst, c[j]);
+      for (int st = 0; st < 8; ++st) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (slot >= 0) v = *reinterpret_cast<const u32x4*>(p + (st >> 2) * 128 + 32 * (st & 3));
+        a[kb][st] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  };
+
+  // transpose-read bases of the B operand ([q ; dout] rows x dims) per dim block db:
+  // source lane m of lane group G reads row 8 (G / 2) + m / 4 (+ 16 st, + 4 for the
+  // second read), dims 128 wb + 32 db + 16 (G % 2) + 4 (m % 4)
+  const int G = lane >> 4, m = lane & 15;
+  int boff[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int row = 8 * (G >> 1) + (m >> 2);
+    const int c = 16 * wb + 4 * db + 2 * (G & 1) + ((m & 3) >> 1);
+    boff[db] = row * kYRow + ychunk(row, c) * 16 + (m & 1) * 8;
+  }
+
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[kb][db][j] = 0.f;
+  bool used[2] = {false, false};
+
+  bf16x8 a[2][8], an[2][8];
+  bool act[2], actn[2];
+  Raw raw1 = load_raw(i0);
+  load_rows(i0, raw1, a, act);
+  stage(i0, 0);
+  if (i0 + 1 < i1) raw1 = load_raw(i0 + 1);
+  for (int i = i0; i < i1; ++i) {
+    const int bf = (i - i0) & 1;
+    // this wavefront's staged rows and A rows of query i, and the inputs of query i + 1, landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    tile_barrier();  // every wavefront's rows landed; ybuf[bf ^ 1] is free
+    Raw raw2 = raw1;
+    if (i + 1 < i1) {
+      stage(i + 1, bf ^ 1);
+      load_rows(i + 1, raw1, an, actn);
+      if (i + 2 < i1) raw2 = load_raw(i + 2);
+    }
+    used[0] |= act[0];
+    used[1] |= act[1];
+    if (act[0] || act[1]) {
+      const unsigned char* y = ybuf + bf * kYBytes;
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 bfr[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16x4 lo = ds_read_tr(y + boff[db] + st * 16 * kYRow);
+          const bf16x4 hi = ds_read_tr(y + boff[db] + st * 16 * kYRow + 4 * kYRow);
+          bfr[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (!act[kb]) continue;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb][st], bfr[db], acc[kb][db], 0, 0, 0);
         }
       }
+    }
+    if (i + 1 < i1) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        act[kb] = actn[kb];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) a[kb][st] = an[kb][st];
+      }
+      raw1 = raw2;
+    }
+  }
+
+  // ---- C (32x32 blocks: lane l holds column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4)
+  float* dst = win ? d_ori : d_cmp;
+  const int col = half * 256 + 128 * wb + (lane & 31);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    if (!used[kb]) continue;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int key = key0 + 64 * wa + 32 * kb + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+      if (key >= key_end) continue;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) atomicAdd(dst + static_cast<long long>(key) * 512 + col + 32 * db, acc[kb][db][j]);
     }
   }
 }
 
 // ----------------------------------------------------------------------------- sinks
 
-__global__ __launch_bounds__(kThreads) void mla_bwd_sink_kernel(const void* ws_base, int Tq, int ntc,
+__global__ __launch_bounds__(kThreads) void mla_bwd_sink_kernel(const void* ws_base, int Tq, int nslot,
                                                                 float* __restrict__ d_sinks) {
   __shared__ float part[kThreads];
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, ntc);
+  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot);
   const int h = static_cast<int>(blockIdx.x);
-  float s = 0.f;
-  for (int k = threadIdx.x; k < Tq; k += kThreads) s += ws.sink_terms[static_cast<long long>(k) * 64 + h];
-  part[threadIdx.x] = s;
+  float acc = 0.f;
+  for (int k = threadIdx.x; k < Tq; k += kThreads) acc += ws.sink_terms[static_cast<long long>(k) * 64 + h];
+  part[threadIdx.x] = acc;
   __syncthreads();
   for (int off = kThreads / 2; off > 0; off >>= 1) {
     if (static_cast<int>(threadIdx.x) < off) part[threadIdx.x] += part[threadIdx.x + off];
@@ -484,23 +691,23 @@ void zero(float* p, long long n, hipStream_t s) {
   hipLaunchKernelGGL(zero_f32_kernel, dim3(blocks), dim3(256), 0, s, p, n);
 }
 
+int slots_per_query(int key_cap) { return (key_cap + kNT - 1) / kNT * kNT; }
+
 }  // namespace
 
 bool mla_bwd_shape_supported(int H, int d, int dtype) { return dtype == 1 && H == 64 && d == 512; }
 
-int mla_bwd_tiles_cap(int key_cap) { return (key_cap + kNT - 1) / kNT; }
-
-size_t mla_bwd_workspace_bytes(int Tq, int key_cap) {
-  return ws_bytes(Tq, mla_bwd_tiles_cap(key_cap));
+size_t mla_bwd_workspace_bytes(int Tq, int key_cap, int nvis_cap) {
+  return ws_bytes(Tq, slots_per_query(key_cap), nvis_cap);
 }
 
 hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
                                  int topk, int Tq, int Tkv, int Tc, const int32_t* cu_q, const int32_t* cu_kv,
                                  const int32_t* cu_cmp, int B, int global_start, int r, int wl, int wr,
-                                 const float* sinks, float scale, const void* out, const float* lse,
-                                 const void* dout, void* dq, float* d_ori, float* d_cmp, float* d_sinks,
-                                 float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap, void* workspace,
-                                 hipStream_t s) {
+                                 int max_seqlen_kv, const float* sinks, float scale, const void* out,
+                                 const float* lse, const void* dout, void* dq, float* d_ori, float* d_cmp,
+                                 float* d_sinks, float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap,
+                                 int nvis_cap, void* workspace, hipStream_t s) {
   const int W = wl + wr + 1;
   zero(d_ori, static_cast<long long>(Tkv) * 512, s);
   zero(d_cmp, static_cast<long long>(Tc) * 512, s);
@@ -509,21 +716,33 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
   if (d_sinks != nullptr && (Tq == 0 || sinks == nullptr)) zero(d_sinks, 64, s);
   if (Tq <= 0) return hipGetLastError();
   if (cmp_idx == nullptr) topk = 0;
-  const int ntc = mla_bwd_tiles_cap(key_cap);
+  // window sides past the stream length change nothing and keep t +- w in range
+  const int wl_c = min(wl, Tkv), wr_c = min(wr, Tkv);
+  const int nslot = slots_per_query(key_cap);
   const auto* q16 = static_cast<const uint16_t*>(q);
   const auto* kv16 = static_cast<const uint16_t*>(ori_kv);
   const auto* c16 = static_cast<const uint16_t*>(cmp_kv);
+  const auto* d16 = static_cast<const uint16_t*>(dout);
   auto prep = (topk <= 2 * kThreads) ? mla_bwd_prep_kernel<2> : mla_bwd_prep_kernel<kMaxTopk / kThreads>;
-  hipLaunchKernelGGL(prep, dim3(Tq), dim3(kThreads), 0, s, q16, kv16, c16, cmp_idx, topk, Tq, Tc, cu_q, cu_kv, cu_cmp,
-                     B, global_start, r, wl, wr, sinks, scale, static_cast<const uint16_t*>(out), lse,
-                     static_cast<const uint16_t*>(dout), workspace, ntc, ori_l1, W, cmp_l1, cmp_slots);
+  hipLaunchKernelGGL(prep, dim3(Tq), dim3(kThreads), 0, s, q16, kv16, c16, cmp_idx, topk, Tq, Tc, cu_q, cu_kv,
+                     cu_cmp, B, global_start, r, wl_c, wr_c, sinks, scale, static_cast<const uint16_t*>(out), lse, d16,
+                     workspace, nslot, nvis_cap, ori_l1, W, cmp_l1, cmp_slots);
   hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3(Tq), dim3(kThreads), 0, s, kv16, c16, Tq,
-                     static_cast<const void*>(workspace), ntc, static_cast<uint16_t*>(dq));
-  hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(Tq), dim3(kThreads), 0, s, q16, static_cast<const uint16_t*>(dout),
-                     Tq, static_cast<const void*>(workspace), ntc, d_ori, d_cmp);
+                     static_cast<const void*>(workspace), nslot, static_cast<uint16_t*>(dq));
+  // dkv: an upper bound of the work items (the exact count needs cu_seqlens on the host)
+  const long long seg_max = max(1, max_seqlen_kv);
+  const long long chunks_w = (min(static_cast<long long>(kGK) + wl_c + wr_c, seg_max) + kQCH - 1) / kQCH;
+  long long items = (static_cast<long long>(Tkv) / kGK + B) * chunks_w;
+  if (cmp_kv != nullptr) items += (static_cast<long long>(Tc) / kGK + B) * ((seg_max + kQCH - 1) / kQCH);
+  items = (items + 7) / 8 * 8;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(static_cast<unsigned>(items), 2), dim3(kThreads), 0, s, q16, d16, Tq,
+                     static_cast<const void*>(workspace), nslot, nvis_cap, cu_q, cu_kv,
+                     cmp_kv != nullptr ? cu_cmp : nullptr, B, global_start, r, wl_c, wr_c, Tc,
+                     cmp_idx != nullptr ? 1 : 0, d_ori, d_cmp);
   if (d_sinks != nullptr && sinks != nullptr)
     hipLaunchKernelGGL(mla_bwd_sink_kernel, dim3(64), dim3(kThreads), 0, s, static_cast<const void*>(workspace), Tq,
-                       ntc, d_sinks);
+                       nslot, d_sinks);
   return hipGetLastError();
 }
 
