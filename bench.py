@@ -2,10 +2,13 @@
 kernel's roofline fraction and the CPU oracle as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload pack16k] [--seed 0] [--no-cpu-baseline]
+                    [--no-backward] [--bwd-steps K]
 
 A step is one whole forward over the 16384-token THD pack with every input
 already resident in HBM: segment indices, compression of the latent KV and of
 the indexer keys, lightning indexer + top-k, sparse MLA.  Prints one JSON line.
+After the timed forward steps, a "backward" object times the sparse-MLA backward on
+the same pack (outside the forward's timed region).
 """
 from __future__ import annotations
 
@@ -133,6 +136,60 @@ def cpu_baseline(pack, budget_s=15.0):
                       f"extrapolated per query to the whole pack"}
 
 
+def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
+    """csa_sparse_mla_bwd on the forward's output and lse with a seeded bf16 dout.
+
+    Algorithmic work: five products of 64 heads x 512 dims per attended (query, key)
+    pair (S and dP recomputed, dq, and the two row-gradient terms), 10 H d flops."""
+    import torch
+    from sparse_attention_thd_amd import _lib
+    L = plan.L
+    cmp_idx = plan.topk_idx
+    topk = plan.topk if cmp_idx is not None else 0
+    lse = torch.empty((pack.Tq, pack.H), dtype=torch.float32, device="cuda")
+    _lib.csa_sparse_mla_fwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx, topk, L.Tq, L.Tkv, plan.H, plan.d,
+                            L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r,
+                            plan.wl, plan.wr, inputs["sinks"], plan.scale, plan.out, lse)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    dout = torch.randn(plan.out.shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    Tc = plan.cmp_kv.shape[0] if plan.cmp_kv is not None else 0
+    W = plan.wl + plan.wr + 1
+    if cmp_idx is not None:
+        slots = topk
+    else:
+        slots = max(1, L.max_seqlen_kv // plan.r) if plan.cmp_kv is not None else 0
+    nbytes = _lib.csa_sparse_mla_bwd_workspace_bytes(L.Tq, plan.wl, plan.wr, plan.cmp_kv, cmp_idx, topk,
+                                                     L.max_seqlen_kv, plan.r)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    dq = torch.empty_like(plan.out)
+    d_ori = torch.empty((L.Tkv, plan.d), dtype=torch.float32, device="cuda")
+    d_cmp = torch.empty((Tc, plan.d), dtype=torch.float32, device="cuda") if Tc else None
+    d_sinks = torch.empty(plan.H, dtype=torch.float32, device="cuda")
+    ori_l1 = torch.empty((L.Tq, W), dtype=torch.float32, device="cuda")
+    cmp_l1 = torch.empty((L.Tq, slots), dtype=torch.float32, device="cuda") if slots else None
+
+    def bwd():
+        _lib.csa_sparse_mla_bwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx, topk, L.Tq, L.Tkv, Tc, plan.H,
+                                plan.d, L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start,
+                                plan.r, plan.wl, plan.wr, L.max_seqlen_kv, inputs["sinks"], plan.scale, plan.out, lse,
+                                dout, dq, d_ori, d_cmp, d_sinks, ori_l1, cmp_l1, slots, ws)
+
+    for _ in range(warmup):
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(); bwd(); e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 10.0 * pack.H * pack.d * (nwin + ncmp)
+    return {"call": "csa_sparse_mla_bwd (dq, d_ori_kv, d_cmp_kv, d_sinks, ori/cmp softmax_l1_norm)",
+            "steps": steps, "avg_call_ms": ms, "tokens_per_s": pack.Tq / (ms / 1e3),
+            "algorithmic_flops_per_call": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12,
+            "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +199,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-backward", action="store_true", help="skip the sparse-MLA backward measurement")
+    ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -259,6 +318,8 @@ def main():
                     "mfma_frac": (idx_flops / (idx_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS) if idx_ms > 0 else None},
         "host_wall_s": wall,
     }
+    if not args.no_backward and pack.H == 64 and pack.d == 512:
+        result["backward"] = backward_bench(plan, pack, inputs, nwin, ncmp, args.bwd_steps, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pack, args.cpu_budget)
     print(json.dumps(result), flush=True)

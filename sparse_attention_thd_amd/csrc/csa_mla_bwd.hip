@@ -399,30 +399,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 // ----------------------------------------------------------------------------- dkv
 
-// Work items, per segment: window tiles (128 key rows) x query chunks of the tile's band,
-// then compressed tiles (128 compressed rows) x query chunks of the segment.  The counts
-// depend only on cu_seqlens, so every workgroup derives the item list itself.
-struct SegItems {
-  int nw, chunks_w, tiles_c, chunks_c;
+// Work items.  The queries of a segment are cut into chunks of 128; a chunk's group
+// holds the window tiles (128 latent rows from the segment start) that its queries
+// see and the compressed tiles (128 rows) visible to its last query, each in two dims
+// halves.  All items of a group stream the same q / dout rows, so a group runs on one
+// XCD at one time and those rows come from HBM about once.
+struct ChunkGroup {
+  int T0, T1;       // stream rows of the chunk's first and last query
+  int m_lo, n_w;    // window tiles m_lo .. m_lo + n_w - 1
+  int n_c;          // compressed tiles 0 .. n_c - 1
 };
 
-__device__ __forceinline__ SegItems seg_items(int b, int B, const int32_t* __restrict__ cu_q,
-                                              const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
-                                              int wl, int wr, int Tc) {
-  SegItems it = {0, 0, 0, 0};
-  if (b >= B) return it;
-  const int L = cu_kv[b + 1] - cu_kv[b];
-  const int Lq = cu_q[b + 1] - cu_q[b];
-  if (L <= 0 || Lq <= 0) return it;
-  const long long band = static_cast<long long>(kGK) + wl + wr;
-  it.chunks_w = static_cast<int>((min(band, static_cast<long long>(Lq)) + kQCH - 1) / kQCH);
-  it.nw = (L + kGK - 1) / kGK * it.chunks_w;
+__device__ __forceinline__ ChunkGroup chunk_group(int b, int c, const int32_t* __restrict__ cu_q,
+                                                  const int32_t* __restrict__ cu_kv,
+                                                  const int32_t* __restrict__ cu_cmp, int global_start, int r,
+                                                  int wl, int wr, int Tc) {
+  ChunkGroup gr;
+  const int s = cu_kv[b], e = cu_kv[b + 1];
+  const int qa = cu_q[b], qb = cu_q[b + 1];
+  gr.T0 = global_start + qa + kQCH * c;
+  gr.T1 = global_start + min(qb, qa + kQCH * (c + 1)) - 1;
+  const int lo_key = max(s, gr.T0 - wl), hi_key = min(e - 1, gr.T1 + wr);
+  gr.m_lo = (lo_key - s) / kGK;
+  gr.n_w = (lo_key <= hi_key) ? (hi_key - s) / kGK - gr.m_lo + 1 : 0;
+  gr.n_c = 0;
   if (cu_cmp != nullptr) {
     const int Lc = max(0, min(cu_cmp[b + 1], Tc) - cu_cmp[b]);
-    it.tiles_c = (Lc + kGK - 1) / kGK;
-    it.chunks_c = (Lq + kQCH - 1) / kQCH;
+    const int nvis = min((gr.T1 - s + 1) / r, Lc);
+    gr.n_c = (nvis + kGK - 1) / kGK;
   }
-  return it;
+  return gr;
+}
+
+__device__ __forceinline__ int seg_chunks(int b, const int32_t* __restrict__ cu_q,
+                                          const int32_t* __restrict__ cu_kv) {
+  const int Lq = cu_q[b + 1] - cu_q[b];
+  return (Lq > 0 && cu_kv[b + 1] > cu_kv[b]) ? (Lq + kQCH - 1) / kQCH : 0;
 }
 
 __device__ __forceinline__ int wave_incl_scan(int x) {
@@ -449,65 +461,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wa = wave >> 1, wb = wave & 1;  // key half and dims half of the workgroup tile
-  const int half = static_cast<int>(blockIdx.y);
 
-  // ---- the work item of this workgroup; consecutive items go to one XCD (the hardware
-  // deals workgroups to the 8 XCDs round robin), so neighbouring tiles share q / dout in L2
-  int total = 0;
-  for (int base = 0; base < B; base += 64) {
-    const SegItems it = seg_items(base + lane, B, cu_q, cu_kv, cu_cmp, wl, wr, Tc);
-    int c = it.nw + it.tiles_c * it.chunks_c;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, 64);
-    total += c;
-  }
-  total = __builtin_amdgcn_readfirstlane(total);
-  const int per = (total + 7) / 8;
+  // ---- the work item of this workgroup.  The hardware deals workgroups to the 8 XCDs
+  // round robin (workgroup x to XCD x % 8, in order), so group g goes to XCD g % 8 and
+  // takes consecutive workgroup slots there: two per item (the dims halves).
   const int x = static_cast<int>(blockIdx.x);
-  if (x / 8 >= per) return;
-  const int item = (x % 8) * per + x / 8;
-  if (item >= total) return;
-  int seg = -1, u = 0, run = 0;
-  for (int base = 0; base < B && seg < 0; base += 64) {
-    const SegItems it = seg_items(base + lane, B, cu_q, cu_kv, cu_cmp, wl, wr, Tc);
-    const int c = it.nw + it.tiles_c * it.chunks_c;
-    const int incl = wave_incl_scan(c) + run;
-    const unsigned long long hit = __ballot(incl - c <= item && item < incl && c > 0);
-    if (hit != 0ull) {
-      const int src = __builtin_ctzll(hit);
-      seg = base + src;
-      u = item - __shfl(incl - c, src, 64);
+  const int xcd = x & 7, slot = x >> 3;
+  int seg = -1, chunk = 0, local = 0, off = 0, g_base = 0;
+  for (int b = 0; b < B && seg < 0; ++b) {
+    const int nch = seg_chunks(b, cu_q, cu_kv);
+    for (int cbase = 0; cbase < nch && seg < 0; cbase += 64) {
+      const int c = cbase + lane;
+      int v = 0;
+      if (c < nch && ((g_base + c) & 7) == xcd) {
+        const ChunkGroup gr = chunk_group(b, c, cu_q, cu_kv, cu_cmp, global_start, r, wl, wr, Tc);
+        v = 2 * (gr.n_w + gr.n_c);
+      }
+      const int incl = wave_incl_scan(v) + off;
+      const unsigned long long hit = __ballot(v > 0 && incl - v <= slot && slot < incl);
+      if (hit != 0ull) {
+        const int src = __builtin_ctzll(hit);
+        seg = b;
+        chunk = cbase + src;
+        local = slot - __shfl(incl - v, src, 64);
+      }
+      off = __shfl(incl, 63, 64);
     }
-    run = __shfl(incl, 63, 64);
+    g_base += nch;
   }
   seg = __builtin_amdgcn_readfirstlane(seg);
-  u = __builtin_amdgcn_readfirstlane(u);
   if (seg < 0) return;
-  const SegItems it = seg_items(seg, B, cu_q, cu_kv, cu_cmp, wl, wr, Tc);
+  chunk = __builtin_amdgcn_readfirstlane(chunk);
+  local = __builtin_amdgcn_readfirstlane(local);
+  const ChunkGroup gr = chunk_group(seg, chunk, cu_q, cu_kv, cu_cmp, global_start, r, wl, wr, Tc);
+  const int half = local & 1, u = local >> 1;
   const int s = cu_kv[seg], e = cu_kv[seg + 1];
-  const int qa = cu_q[seg], qb = cu_q[seg + 1];
-  const bool win = u < it.nw;
+  const bool win = u < gr.n_w;
   int key0, key_end, i0, i1, cb = 0, nvis_seg = 0;
   if (win) {
-    const int tile = u / it.chunks_w, chunk = u % it.chunks_w;
-    key0 = s + kGK * tile;
+    key0 = s + kGK * (gr.m_lo + u);
     key_end = min(key0 + kGK, e);
-    const int band_lo = max(key0 - wr, global_start + qa);
-    const int band_hi = min(key_end - 1 + wl, global_start + qb - 1);
-    i0 = band_lo - global_start + chunk * kQCH;
-    i1 = min(band_hi - global_start + 1, i0 + kQCH);
+    i0 = max(gr.T0, key0 - wr) - global_start;
+    i1 = min(gr.T1, key_end - 1 + wl) - global_start + 1;
   } else {
-    const int v = u - it.nw;
-    const int chunk = v / it.tiles_c, tile = v % it.tiles_c;
     cb = cu_cmp[seg];
     nvis_seg = min(cu_cmp[seg + 1], Tc) - cb;
-    key0 = cb + kGK * tile;
+    key0 = cb + kGK * (u - gr.n_w);
     key_end = min(key0 + kGK, cb + nvis_seg);
-    i0 = qa + chunk * kQCH;
-    i1 = min(qb, i0 + kQCH);
     // the first query that sees row key0 sits at segment position (key0 - cb + 1) r - 1
-    const long long first = static_cast<long long>(s) + static_cast<long long>(key0 - cb + 1) * r - 1 - global_start;
-    if (first > i0) i0 = static_cast<int>(min(first, static_cast<long long>(i1)));
+    const long long first = static_cast<long long>(s) + static_cast<long long>(key0 - cb + 1) * r - 1;
+    i0 = static_cast<int>(max(static_cast<long long>(gr.T0), first)) - global_start;
+    i1 = gr.T1 - global_start + 1;
   }
   if (i0 >= i1) return;
 
@@ -601,54 +605,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int j = 0; j < 16; ++j) acc[kb][db][j] = 0.f;
   bool used[2] = {false, false};
 
+  // One query per step: wait for its staged rows and A rows, start staging and A loads
+  // of the next query and the inputs of the one after, then the MFMAs.  Two register
+  // sets alternate between steps, so the prefetched A rows are first waited for at the
+  // top of the next step.
   bf16x8 a[2][8], an[2][8];
   bool act[2], actn[2];
   Raw raw1 = load_raw(i0);
   load_rows(i0, raw1, a, act);
   stage(i0, 0);
   if (i0 + 1 < i1) raw1 = load_raw(i0 + 1);
-  for (int i = i0; i < i1; ++i) {
+  auto step = [&](int i, bf16x8 (&ac)[2][8], const bool (&actc)[2], bf16x8 (&ax)[2][8], bool (&actx)[2]) {
     const int bf = (i - i0) & 1;
-    // this wavefront's staged rows and A rows of query i, and the inputs of query i + 1, landed
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    tile_barrier();  // every wavefront's rows landed; ybuf[bf ^ 1] is free
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // rows of query i and the inputs of query i + 1 landed
+    tile_barrier();                      // every wavefront's rows landed; ybuf[bf ^ 1] is free
     Raw raw2 = raw1;
     if (i + 1 < i1) {
       stage(i + 1, bf ^ 1);
-      load_rows(i + 1, raw1, an, actn);
+      load_rows(i + 1, raw1, ax, actx);
       if (i + 2 < i1) raw2 = load_raw(i + 2);
     }
-    used[0] |= act[0];
-    used[1] |= act[1];
-    if (act[0] || act[1]) {
+    used[0] |= actc[0];
+    used[1] |= actc[1];
+    if (actc[0] || actc[1]) {
       const unsigned char* y = ybuf + bf * kYBytes;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        bf16x8 bfr[4];
+      // B fragments of step st + 1 are read while the MFMAs of step st run
+      auto read_b = [&](int st, bf16x8 (&bfr)[4]) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const bf16x4 lo = ds_read_tr(y + boff[db] + st * 16 * kYRow);
           const bf16x4 hi = ds_read_tr(y + boff[db] + st * 16 * kYRow + 4 * kYRow);
           bfr[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+      };
+      bf16x8 bcur[4], bnxt[4];
+      read_b(0, bcur);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (st + 1 < 8) read_b(st + 1, bnxt);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if (!act[kb]) continue;
+          if (!actc[kb]) continue;
 #pragma unroll
           for (int db = 0; db < 4; ++db)
-            acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb][st], bfr[db], acc[kb][db], 0, 0, 0);
+            acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[kb][st], bcur[db], acc[kb][db], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) bcur[db] = bnxt[db];
       }
     }
-    if (i + 1 < i1) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        act[kb] = actn[kb];
-#pragma unroll
-        for (int st = 0; st < 8; ++st) a[kb][st] = an[kb][st];
-      }
-      raw1 = raw2;
-    }
+    raw1 = raw2;
+  };
+  for (int i = i0; i < i1; i += 2) {
+    step(i, a, act, an, actn);
+    if (i + 1 < i1) step(i + 1, an, actn, a, act);
   }
 
   // ---- C (32x32 blocks: lane l holds column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4)
@@ -729,14 +740,15 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
                      workspace, nslot, nvis_cap, ori_l1, W, cmp_l1, cmp_slots);
   hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3(Tq), dim3(kThreads), 0, s, kv16, c16, Tq,
                      static_cast<const void*>(workspace), nslot, static_cast<uint16_t*>(dq));
-  // dkv: an upper bound of the work items (the exact count needs cu_seqlens on the host)
+  // dkv: an upper bound of the workgroup slots per XCD (the exact count needs cu_seqlens
+  // on the host): groups <= Tq / 128 + B, each with at most n_w + n_c items x 2 halves
   const long long seg_max = max(1, max_seqlen_kv);
-  const long long chunks_w = (min(static_cast<long long>(kGK) + wl_c + wr_c, seg_max) + kQCH - 1) / kQCH;
-  long long items = (static_cast<long long>(Tkv) / kGK + B) * chunks_w;
-  if (cmp_kv != nullptr) items += (static_cast<long long>(Tc) / kGK + B) * ((seg_max + kQCH - 1) / kQCH);
-  items = (items + 7) / 8 * 8;
+  const long long groups = (static_cast<long long>(Tq) + kQCH - 1) / kQCH + B;
+  const long long n_w = (min(static_cast<long long>(kQCH) + wl_c + wr_c - 1, seg_max) + kGK - 1) / kGK + 1;
+  const long long n_c = (cmp_kv != nullptr) ? (seg_max / r + kGK - 1) / kGK : 0;
+  const long long items = (groups + 7) / 8 * 2 * (n_w + n_c) * 8;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(static_cast<unsigned>(items), 2), dim3(kThreads), 0, s, q16, d16, Tq,
+  hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(static_cast<unsigned>(items)), dim3(kThreads), 0, s, q16, d16, Tq,
                      static_cast<const void*>(workspace), nslot, nvis_cap, cu_q, cu_kv,
                      cmp_kv != nullptr ? cu_cmp : nullptr, B, global_start, r, wl_c, wr_c, Tc,
                      cmp_idx != nullptr ? 1 : 0, d_ori, d_cmp);
