@@ -27,11 +27,15 @@ namespace csa {
 namespace {
 
 constexpr int kSlotBytes = 256;  // scale * dS (bytes 0..127) then P (128..255), 64 heads bf16 each
-constexpr int kGK = 128;         // keys per dkv tile
-constexpr int kQCH = 128;        // queries per dkv work item
-constexpr int kYRow = 512;       // staged q / dout half row: 256 dims
-constexpr int kYBytes = 128 * kYRow;  // 64 q rows then 64 dout rows of one query
 constexpr int kDsStride = 144;   // staged dS row of the dq pass (128 bytes + pad)
+// row-gradient (dkv) pass
+constexpr int kGK = 256;                // keys per tile
+constexpr int kQCH = 128;               // queries per chunk
+constexpr int kDkvThreads = 512;        // 8 wavefronts
+constexpr int kYRow = 512;              // staged q or dout row: 256 dims
+constexpr int kYChunk = 64 * kYRow;     // one term's 64 head rows of one query
+constexpr int kAChunk = kGK * 128;      // one term's 64 heads of the tile's keys
+constexpr int kStage = kYChunk + kAChunk;  // one (query, term) stage: 64 KiB
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -41,14 +45,16 @@ struct BwdWorkspace {
   float* sink_terms;     // [Tq][64]
   int32_t* nkeys;        // [Tq]
   int16_t* cmap;         // [Tq][nvis_cap] compacted index of each visible compressed row, -1 if not selected
+  unsigned char* zero;   // one slot row of zeros (the A rows of keys a query does not attend)
 };
 
 __host__ __device__ inline size_t ws_bytes(long long Tq, int nslot, int nvis_cap) {
-  return static_cast<size_t>(Tq) *
-         (static_cast<size_t>(nslot) * (kSlotBytes + 4) + 64 * 4 + 4 + static_cast<size_t>(nvis_cap) * 2);
+  const size_t head = static_cast<size_t>(Tq) *
+                      (static_cast<size_t>(nslot) * (kSlotBytes + 4) + 64 * 4 + 4 + static_cast<size_t>(nvis_cap) * 2);
+  return (head + 15) / 16 * 16 + kSlotBytes;  // + one zero slot row
 }
 
-__host__ __device__ inline BwdWorkspace ws_layout(void* base, long long Tq, int nslot) {
+__host__ __device__ inline BwdWorkspace ws_layout(void* base, long long Tq, int nslot, int nvis_cap) {
   BwdWorkspace w;
   unsigned char* p = static_cast<unsigned char*>(base);
   w.slots = p;
@@ -60,6 +66,7 @@ __host__ __device__ inline BwdWorkspace ws_layout(void* base, long long Tq, int 
   w.nkeys = reinterpret_cast<int32_t*>(p);
   p += static_cast<size_t>(Tq) * 4;
   w.cmap = reinterpret_cast<int16_t*>(p);
+  w.zero = static_cast<unsigned char*>(base) + ws_bytes(Tq, nslot, nvis_cap) - kSlotBytes;
   return w;
 }
 
@@ -137,7 +144,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int n = lane & 15, g = lane >> 4;
   const int head = 16 * wave + n;
   const bool sparse = cmp_kv != nullptr && cmp_idx != nullptr;
-  const BwdWorkspace ws = ws_layout(ws_base, Tq, nslot);
+  const BwdWorkspace ws = ws_layout(ws_base, Tq, nslot, nvis_cap);
   const float scale_log2 = scale * kLog2e;
 
   int vals[NC];
@@ -179,6 +186,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int nkeys = min(qk.nwin + qk.ncmp, nslot);  // the workspace holds nslot keys per query
   const int ntiles = (nkeys + kNT - 1) / kNT;
   if (tid == 0) ws.nkeys[i] = nkeys;
+  if (i == 0 && tid < kSlotBytes / 16) reinterpret_cast<u32x4*>(ws.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
   if (sinks != nullptr && g == 0)
     ws.sink_terms[static_cast<long long>(i) * 64 + head] = -exp2f(sinks[head] * kLog2e - lse2_h) * Dh;
   // Map of the visible compressed rows for the key-major dkv pass (sparse mode): the
@@ -307,7 +315,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_dq_kernel(
     const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv, int Tq, const void* ws_base, int nslot,
-    uint16_t* __restrict__ dq) {
+    int nvis_cap, uint16_t* __restrict__ dq) {
   __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char dsb[2][kNT * kDsStride];
   const int i = static_cast<int>(blockIdx.x);
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot);
+  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot, nvis_cap);
   const int nkeys = __builtin_amdgcn_readfirstlane(ws.nkeys[i]);
   const int ntiles = (nkeys + kNT - 1) / kNT;
   const int32_t* codes = ws.codes + static_cast<long long>(i) * nslot;
@@ -400,14 +408,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 // ----------------------------------------------------------------------------- dkv
 
 // Work items.  The queries of a segment are cut into chunks of 128; a chunk's group
-// holds the window tiles (128 latent rows from the segment start) that its queries
-// see and the compressed tiles (128 rows) visible to its last query, each in two dims
-// halves.  All items of a group stream the same q / dout rows, so a group runs on one
-// XCD at one time and those rows come from HBM about once.
+// holds the window tiles (256 latent rows from the first row its queries see) and the
+// compressed tiles (256 rows) visible to its last query, each in two dims halves.  All
+// items of a group stream the same q / dout rows, so a group takes consecutive
+// workgroup slots on one XCD.
 struct ChunkGroup {
-  int T0, T1;       // stream rows of the chunk's first and last query
-  int m_lo, n_w;    // window tiles m_lo .. m_lo + n_w - 1
-  int n_c;          // compressed tiles 0 .. n_c - 1
+  int T0, T1;  // stream rows of the chunk's first and last query
+  int k_lo;    // first window row of the chunk
+  int k_hi;    // last window row of the chunk
+  int n_w;     // window tiles k_lo + 256 j
+  int n_c;     // compressed tiles 0 .. n_c - 1
 };
 
 __device__ __forceinline__ ChunkGroup chunk_group(int b, int c, const int32_t* __restrict__ cu_q,
@@ -419,9 +429,9 @@ __device__ __forceinline__ ChunkGroup chunk_group(int b, int c, const int32_t* _
   const int qa = cu_q[b], qb = cu_q[b + 1];
   gr.T0 = global_start + qa + kQCH * c;
   gr.T1 = global_start + min(qb, qa + kQCH * (c + 1)) - 1;
-  const int lo_key = max(s, gr.T0 - wl), hi_key = min(e - 1, gr.T1 + wr);
-  gr.m_lo = (lo_key - s) / kGK;
-  gr.n_w = (lo_key <= hi_key) ? (hi_key - s) / kGK - gr.m_lo + 1 : 0;
+  gr.k_lo = max(s, gr.T0 - wl);
+  gr.k_hi = min(e - 1, gr.T1 + wr);
+  gr.n_w = (gr.k_lo <= gr.k_hi) ? (gr.k_hi - gr.k_lo) / kGK + 1 : 0;
   gr.n_c = 0;
   if (cu_cmp != nullptr) {
     const int Lc = max(0, min(cu_cmp[b + 1], Tc) - cu_cmp[b]);
@@ -447,24 +457,44 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
   return x;
 }
 
-// Staged q / dout rows: row r (q head r, or dout head r - 64), 16-byte chunk c of the
-// 256-dim half lives at chunk c ^ (4 (r % 4)), so that the transpose reads of one
-// half-wavefront (4 rows x 4 chunks) touch every bank once.
+// Staged q / dout rows (64 heads x 256 dims): 16-byte chunk c of row r lives at chunk
+// c ^ (4 (r % 4)), so that the transpose reads of a half-wavefront (4 rows x 4 chunks)
+// touch every bank once.
 __device__ __forceinline__ int ychunk(int row, int c) { return c ^ (4 * (row & 3)); }
+// Staged A rows (tile keys x 64 heads of one term, 128 bytes): chunk c of key row r at
+// chunk c ^ ((r / 2) % 8), so that 16 lanes reading 16 bytes of 16 consecutive keys touch
+// every bank once.
+__device__ __forceinline__ int achunk(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mla_bwd_dkv_kernel(
+// 16 bytes per lane from a per-lane address into LDS at M0 + 16 lane (wave-uniform base).
+__device__ __forceinline__ void gather_to_lds(const void* src, uint32_t lds_off) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_off), "v"(src)
+      : "memory", "m0");
+}
+
+// C[tile keys x 256 dims] += sum over the item's queries i and (term, head) k of
+// A[key, k] Y[k, dim]: A = scale dS (term 0) or P (term 1) of pair (i, key) from its slot
+// row, Y = q or dout of query i.  Each (query, term) is one 64 KiB stage in LDS: the 64
+// head rows of Y and the 256 keys' A rows, both loaded with global_load_lds.  Wavefront
+// (a, b) owns key blocks a and a + 4 (32 keys each) and dims 128 b .. of the half.
+__global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_dkv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, int Tq, const void* ws_base, int nslot,
     int nvis_cap, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
     const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr, int Tc, int sparse,
     float* __restrict__ d_ori, float* __restrict__ d_cmp) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ybuf[2 * kYBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char stg[2 * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wa = wave >> 1, wb = wave & 1;  // key half and dims half of the workgroup tile
+  const int wa = wave & 3, wb = wave >> 2;
 
-  // ---- the work item of this workgroup.  The hardware deals workgroups to the 8 XCDs
-  // round robin (workgroup x to XCD x % 8, in order), so group g goes to XCD g % 8 and
-  // takes consecutive workgroup slots there: two per item (the dims halves).
+  // ---- the work item.  The hardware deals workgroups to the 8 XCDs round robin
+  // (workgroup x to XCD x % 8, in order), so group g goes to XCD g % 8 and takes
+  // consecutive workgroup slots there: two per item (the dims halves).
   const int x = static_cast<int>(blockIdx.x);
   const int xcd = x & 7, slot = x >> 3;
   int seg = -1, chunk = 0, local = 0, off = 0, g_base = 0;
@@ -499,8 +529,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const bool win = u < gr.n_w;
   int key0, key_end, i0, i1, cb = 0, nvis_seg = 0;
   if (win) {
-    key0 = s + kGK * (gr.m_lo + u);
-    key_end = min(key0 + kGK, e);
+    key0 = gr.k_lo + kGK * u;
+    key_end = min(key0 + kGK, gr.k_hi + 1);
     i0 = max(gr.T0, key0 - wr) - global_start;
     i1 = min(gr.T1, key_end - 1 + wl) - global_start + 1;
   } else {
@@ -515,78 +545,82 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
   if (i0 >= i1) return;
 
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot);
-  const uint32_t yb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(ybuf)));
+  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot, nvis_cap);
+  const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(stg)));
 
-  // ---- staging of query i's q and dout (this dims half) into ybuf[bf]: 64 wave
-  // instructions of 1 KiB (two rows each); wavefronts 0, 1 take q, 2, 3 take dout
-  auto stage = [&](int i, int bf) {
-    const uint16_t* src = (wave < 2 ? q : dout) + static_cast<long long>(i) * 64 * 512;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int uu = 16 * wave + v;
-      const int row = 2 * uu + (lane >> 5);
-      const uint32_t off = static_cast<uint32_t>((row & 63) * 1024 + half * 512 + ychunk(row, lane & 31) * 16);
-      row_to_lds(src, off, yb + static_cast<uint32_t>(bf * kYBytes + uu * 1024));
-    }
+  // ---- per-query key window: rows [lo, lo + nwin) of the segment; nk keys in the workspace
+  struct QInfo {
+    int lo, hi, nwin, vis, nk;
   };
-  // ---- A operand (keys x (term, head)) of query i: lane l holds key 32 kb + l % 32 of
-  // this wavefront's 64, k-slots 8 (l / 32) .. of step st = 4 term + head block.  Three
-  // steps, pipelined one query apart: the per-query inputs (slot count, selection-map
-  // entries), the slots, the slot rows.
-  struct Raw {
-    int nk;      // keys of the query in the workspace
-    int map[2];  // selection-map entry of this lane's key per key block (sparse compressed items)
-  };
-  auto load_raw = [&](int i) {
-    Raw w;
+  auto qinfo = [&](int i) {
+    QInfo w;
+    const int t = global_start + i;
+    w.lo = max(s, t - wl);
+    w.hi = min(e - 1, t + wr);
+    w.nwin = w.hi - w.lo + 1;
+    w.vis = win ? 0 : min((t - s + 1) / r, nvis_seg);
     w.nk = ws.nkeys[i];
-    w.map[0] = w.map[1] = -1;
+    return w;
+  };
+  // this lane's 4 tile keys in the A staging: key rows 32 wave + 8 v + lane / 8
+  auto key_of = [&](int v) { return 32 * wave + 8 * v + (lane >> 3); };
+  // selection-map entries of this lane's 4 keys for query i (sparse compressed items)
+  auto load_map = [&](int i, int (&mp)[4]) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) mp[v] = -1;
     if (!win && sparse) {
       const int t = global_start + i;
       const int vis = min(min((t - s + 1) / r, nvis_seg), nvis_cap);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int v = key0 + 64 * wa + 32 * kb + (lane & 31) - cb;
-        if (v < vis) w.map[kb] = ws.cmap[static_cast<long long>(i) * nvis_cap + v];
+      for (int v = 0; v < 4; ++v) {
+        const int vv = key0 + key_of(v) - cb;
+        if (vv < vis) mp[v] = ws.cmap[static_cast<long long>(i) * nvis_cap + vv];
       }
     }
-    return w;
   };
-  auto load_rows = [&](int i, const Raw& w, bf16x8 (&a)[2][8], bool (&act)[2]) {
-    const int t = global_start + i;
-    const int lo = max(s, t - wl);
-    const int nwin = min(e - 1, t + wr) - lo + 1;
-    const int vis = win ? 0 : min((t - s + 1) / r, nvis_seg);
+  // slot row base of this lane's 4 keys for query i (the zero row where i does not attend)
+  auto slot_rows = [&](int i, const QInfo& w, const int (&mp)[4], const unsigned char* (&rowp)[4]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = key0 + 64 * wa + 32 * kb + (lane & 31);
-      int slot = -1;
+    for (int v = 0; v < 4; ++v) {
+      const int key = key0 + key_of(v);
+      int sl = -1;
       if (key < key_end) {
         if (win) {
-          slot = key - lo;
-          if (slot >= nwin) slot = -1;
-        } else if (key - cb < vis) {
-          const int j = sparse ? w.map[kb] : key - cb;
-          slot = (j >= 0) ? nwin + j : -1;
+          if (key >= w.lo && key <= w.hi) sl = key - w.lo;
+        } else if (key - cb < w.vis) {
+          const int j = sparse ? mp[v] : key - cb;
+          sl = (j >= 0) ? w.nwin + j : -1;
         }
-        if (slot >= w.nk) slot = -1;
+        if (sl >= w.nk) sl = -1;
       }
-      act[kb] = __ballot(slot >= 0) != 0ull;
-      const unsigned char* p =
-          ws.slots + (static_cast<long long>(i) * nslot + max(slot, 0)) * kSlotBytes + 16 * (lane >> 5);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (slot >= 0) v = *reinterpret_cast<const u32x4*>(p + (st >> 2) * 128 + 32 * (st & 3));
-        a[kb][st] = __builtin_bit_cast(bf16x8, v);
-      }
+      rowp[v] = (sl >= 0) ? ws.slots + (static_cast<long long>(i) * nslot + sl) * kSlotBytes : ws.zero;
     }
   };
+  // one (query, term) stage into buffer bf: Y rows (4 instructions per wavefront, 2 rows of
+  // 512 bytes each) then A rows (4 instructions, 8 keys of 128 bytes each)
+  auto stage = [&](int i, int term, const unsigned char* const (&rowp)[4], int bf) {
+    const uint16_t* ysrc = (term ? dout : q) + static_cast<long long>(i) * 64 * 512;
+    const uint32_t base = sb + static_cast<uint32_t>(bf * kStage);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int uu = 4 * wave + v;
+      const int row = 2 * uu + (lane >> 5);
+      const uint32_t yoff = static_cast<uint32_t>(row * 1024 + half * 512 + ychunk(row, lane & 31) * 16);
+      row_to_lds(ysrc, yoff, base + static_cast<uint32_t>(uu * 1024));
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int kk = key_of(v);
+      gather_to_lds(rowp[v] + term * 128 + achunk(kk, lane & 7) * 16,
+                    base + static_cast<uint32_t>(kYChunk + (8 * wave + 2 * v) * 512));
+    }
+  };
+  // Wait: the A instruction of (wave, v) covers keys 8 (4 wave + v) .. + 7, i.e. 1 KiB at
+  // kYChunk + (4 wave + v) * 1024 = kYChunk + (8 wave + 2 v) * 512.  key_of(v) matches.
 
-  // transpose-read bases of the B operand ([q ; dout] rows x dims) per dim block db:
-  // source lane m of lane group G reads row 8 (G / 2) + m / 4 (+ 16 st, + 4 for the
-  // second read), dims 128 wb + 32 db + 16 (G % 2) + 4 (m % 4)
+  // transpose-read bases of Y (B operand) per dim block db: source lane m of lane group G
+  // reads head row 8 (G / 2) + m / 4 (+ 16 st, + 4 for the second read), dims
+  // 128 wb + 32 db + 16 (G % 2) + 4 (m % 4)
   const int G = lane >> 4, m = lane & 15;
   int boff[4];
 #pragma unroll
@@ -594,6 +628,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int row = 8 * (G >> 1) + (m >> 2);
     const int c = 16 * wb + 4 * db + 2 * (G & 1) + ((m & 3) >> 1);
     boff[db] = row * kYRow + ychunk(row, c) * 16 + (m & 1) * 8;
+  }
+  // A reads (16 bytes: key 32 blk + l % 32, heads 16 st + 8 (l / 32) ..) per K step st;
+  // the chunk swizzle of these keys does not depend on the block
+  int aoff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int kk = lane & 31;
+    aoff[st] = kYChunk + (32 * wa + kk) * 128 + achunk(kk, 2 * st + (lane >> 5)) * 16;
   }
 
   f32x16 acc[2][4];
@@ -605,61 +647,70 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       for (int j = 0; j < 16; ++j) acc[kb][db][j] = 0.f;
   bool used[2] = {false, false};
 
-  // One query per step: wait for its staged rows and A rows, start staging and A loads
-  // of the next query and the inputs of the one after, then the MFMAs.  Two register
-  // sets alternate between steps, so the prefetched A rows are first waited for at the
-  // top of the next step.
-  bf16x8 a[2][8], an[2][8];
-  bool act[2], actn[2];
-  Raw raw1 = load_raw(i0);
-  load_rows(i0, raw1, a, act);
-  stage(i0, 0);
-  if (i0 + 1 < i1) raw1 = load_raw(i0 + 1);
-  auto step = [&](int i, bf16x8 (&ac)[2][8], const bool (&actc)[2], bf16x8 (&ax)[2][8], bool (&actx)[2]) {
-    const int bf = (i - i0) & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // rows of query i and the inputs of query i + 1 landed
-    tile_barrier();                      // every wavefront's rows landed; ybuf[bf ^ 1] is free
-    Raw raw2 = raw1;
-    if (i + 1 < i1) {
-      stage(i + 1, bf ^ 1);
-      load_rows(i + 1, raw1, ax, actx);
-      if (i + 2 < i1) raw2 = load_raw(i + 2);
+  // ---- pipeline: stage n + 1 is issued while stage n is multiplied
+  int mp[4];
+  const unsigned char* rowp[4];
+  load_map(i0, mp);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  QInfo cur = qinfo(i0);
+  slot_rows(i0, cur, mp, rowp);
+  stage(i0, 0, rowp, 0);
+  if (i0 + 1 < i1) load_map(i0 + 1, mp);
+  for (int i = i0; i < i1; ++i) {
+    // blocks of this wavefront with attended keys for query i
+    bool act[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k_first = key0 + 32 * (wa + 4 * kb);
+      const int k_last = min(k_first + 31, key_end - 1);
+      act[kb] = win ? (max(k_first, cur.lo) <= min(k_last, cur.hi)) : (k_first < min(cb + cur.vis, key_end));
+      used[kb] |= act[kb];
     }
-    used[0] |= actc[0];
-    used[1] |= actc[1];
-    if (actc[0] || actc[1]) {
-      const unsigned char* y = ybuf + bf * kYBytes;
-      // B fragments of step st + 1 are read while the MFMAs of step st run
-      auto read_b = [&](int st, bf16x8 (&bfr)[4]) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const bf16x4 lo = ds_read_tr(y + boff[db] + st * 16 * kYRow);
-          const bf16x4 hi = ds_read_tr(y + boff[db] + st * 16 * kYRow + 4 * kYRow);
-          bfr[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      };
-      bf16x8 bcur[4], bnxt[4];
-      read_b(0, bcur);
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        if (st + 1 < 8) read_b(st + 1, bnxt);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (!actc[kb]) continue;
-#pragma unroll
-          for (int db = 0; db < 4; ++db)
-            acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ac[kb][st], bcur[db], acc[kb][db], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int db = 0; db < 4; ++db) bcur[db] = bnxt[db];
+    for (int term = 0; term < 2; ++term) {
+      const int n = 2 * (i - i0) + term;
+      const int bf = n & 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // stage n (and the map entries of query i + 1) landed
+      tile_barrier();                      // every wavefront's part landed; buffer bf ^ 1 is free
+      QInfo nxt = cur;
+      if (term == 0) {
+        stage(i, 1, rowp, bf ^ 1);
+      } else if (i + 1 < i1) {
+        nxt = qinfo(i + 1);
+        slot_rows(i + 1, nxt, mp, rowp);
+        stage(i + 1, 0, rowp, bf ^ 1);
+        if (i + 2 < i1) load_map(i + 2, mp);
       }
+      if (act[0] || act[1]) {
+        const unsigned char* y = stg + bf * kStage;
+        auto read_b = [&](int st, bf16x8 (&bfr)[4]) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x4 lo = ds_read_tr(y + boff[db] + st * 16 * kYRow);
+            const bf16x4 hi = ds_read_tr(y + boff[db] + st * 16 * kYRow + 4 * kYRow);
+            bfr[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+        };
+        bf16x8 bcur[4], bnxt[4];
+        read_b(0, bcur);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          if (st + 1 < 4) read_b(st + 1, bnxt);
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            if (!act[kb]) continue;
+            const bf16x8 af = *reinterpret_cast<const bf16x8*>(y + aoff[st] + kb * 4 * 32 * 128);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+              acc[kb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bcur[db], acc[kb][db], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int db = 0; db < 4; ++db) bcur[db] = bnxt[db];
+        }
+      }
+      if (term == 1) cur = nxt;
     }
-    raw1 = raw2;
-  };
-  for (int i = i0; i < i1; i += 2) {
-    step(i, a, act, an, actn);
-    if (i + 1 < i1) step(i + 1, an, actn, a, act);
   }
 
   // ---- C (32x32 blocks: lane l holds column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4)
@@ -670,7 +721,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (!used[kb]) continue;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int key = key0 + 64 * wa + 32 * kb + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+      const int key = key0 + 32 * (wa + 4 * kb) + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
       if (key >= key_end) continue;
 #pragma unroll
       for (int db = 0; db < 4; ++db) atomicAdd(dst + static_cast<long long>(key) * 512 + col + 32 * db, acc[kb][db][j]);
@@ -680,10 +731,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 
 // ----------------------------------------------------------------------------- sinks
 
-__global__ __launch_bounds__(kThreads) void mla_bwd_sink_kernel(const void* ws_base, int Tq, int nslot,
+__global__ __launch_bounds__(kThreads) void mla_bwd_sink_kernel(const void* ws_base, int Tq, int nslot, int nvis_cap,
                                                                 float* __restrict__ d_sinks) {
   __shared__ float part[kThreads];
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot);
+  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot, nvis_cap);
   const int h = static_cast<int>(blockIdx.x);
   float acc = 0.f;
   for (int k = threadIdx.x; k < Tq; k += kThreads) acc += ws.sink_terms[static_cast<long long>(k) * 64 + h];
@@ -739,22 +790,22 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
                      cu_cmp, B, global_start, r, wl_c, wr_c, sinks, scale, static_cast<const uint16_t*>(out), lse, d16,
                      workspace, nslot, nvis_cap, ori_l1, W, cmp_l1, cmp_slots);
   hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3(Tq), dim3(kThreads), 0, s, kv16, c16, Tq,
-                     static_cast<const void*>(workspace), nslot, static_cast<uint16_t*>(dq));
+                     static_cast<const void*>(workspace), nslot, nvis_cap, static_cast<uint16_t*>(dq));
   // dkv: an upper bound of the workgroup slots per XCD (the exact count needs cu_seqlens
   // on the host): groups <= Tq / 128 + B, each with at most n_w + n_c items x 2 halves
   const long long seg_max = max(1, max_seqlen_kv);
   const long long groups = (static_cast<long long>(Tq) + kQCH - 1) / kQCH + B;
-  const long long n_w = (min(static_cast<long long>(kQCH) + wl_c + wr_c - 1, seg_max) + kGK - 1) / kGK + 1;
+  const long long n_w = min(static_cast<long long>(kQCH) - 1 + wl_c + wr_c, seg_max - 1) / kGK + 1;
   const long long n_c = (cmp_kv != nullptr) ? (seg_max / r + kGK - 1) / kGK : 0;
   const long long items = (groups + 7) / 8 * 2 * (n_w + n_c) * 8;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(static_cast<unsigned>(items)), dim3(kThreads), 0, s, q16, d16, Tq,
+  hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(static_cast<unsigned>(items)), dim3(kDkvThreads), 0, s, q16, d16, Tq,
                      static_cast<const void*>(workspace), nslot, nvis_cap, cu_q, cu_kv,
                      cmp_kv != nullptr ? cu_cmp : nullptr, B, global_start, r, wl_c, wr_c, Tc,
                      cmp_idx != nullptr ? 1 : 0, d_ori, d_cmp);
   if (d_sinks != nullptr && sinks != nullptr)
     hipLaunchKernelGGL(mla_bwd_sink_kernel, dim3(64), dim3(kThreads), 0, s, static_cast<const void*>(workspace), Tq,
-                       nslot, d_sinks);
+                       nslot, nvis_cap, d_sinks);
   return hipGetLastError();
 }
 
