@@ -41,7 +41,6 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct BwdWorkspace {
   unsigned char* slots;  // [Tq][nslot][kSlotBytes]
-  int32_t* codes;        // [Tq][nslot] key row of a slot: window row r >= 0, compressed row c -> -1 - c
   float* sink_terms;     // [Tq][64]
   int32_t* nkeys;        // [Tq]
   int16_t* cmap;         // [Tq][nvis_cap] compacted index of each visible compressed row, -1 if not selected
@@ -50,7 +49,7 @@ struct BwdWorkspace {
 
 __host__ __device__ inline size_t ws_bytes(long long Tq, int nslot, int nvis_cap) {
   const size_t head = static_cast<size_t>(Tq) *
-                      (static_cast<size_t>(nslot) * (kSlotBytes + 4) + 64 * 4 + 4 + static_cast<size_t>(nvis_cap) * 2);
+                      (static_cast<size_t>(nslot) * kSlotBytes + 64 * 4 + 4 + static_cast<size_t>(nvis_cap) * 2);
   return (head + 15) / 16 * 16 + kSlotBytes;  // + one zero slot row
 }
 
@@ -59,8 +58,6 @@ __host__ __device__ inline BwdWorkspace ws_layout(void* base, long long Tq, int 
   unsigned char* p = static_cast<unsigned char*>(base);
   w.slots = p;
   p += static_cast<size_t>(Tq) * nslot * kSlotBytes;
-  w.codes = reinterpret_cast<int32_t*>(p);
-  p += static_cast<size_t>(Tq) * nslot * 4;
   w.sink_terms = reinterpret_cast<float*>(p);
   p += static_cast<size_t>(Tq) * 64 * 4;
   w.nkeys = reinterpret_cast<int32_t*>(p);
@@ -122,25 +119,38 @@ __device__ __forceinline__ void load_qstyle(const uint16_t* __restrict__ row, bf
   }
 }
 
-// ----------------------------------------------------------------------------- prep
+// ----------------------------------------------------------------------------- prep + dq
 
+constexpr int kPrepThreads = 512;  // wavefronts 0-3: S and dP; 4-7: the dq product
+
+// One workgroup per query, 8 wavefronts sharing the query's kv tiles in LDS.  Wavefront w
+// (w < 4) forms S and dP for heads 16 w .. 16 w + 15 from q and dout held in registers,
+// writes scale * dS and P of every (query, key) pair as a 256-byte slot row, the
+// tile's dS rows to LDS and the head-averaged probabilities; wavefront 4 + w multiplies
+// those dS rows into dq for the same heads one tile later.  Each SIMD thus runs one
+// wavefront of each kind.
 template <int NC>  // cmp_idx row chunks of kThreads entries
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_prep_kernel(
+__global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv,
     const int32_t* __restrict__ cmp_idx, int topk, int Tq, int Tc, const int32_t* __restrict__ cu_q,
     const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
     int wr, const float* __restrict__ sinks, float scale, const uint16_t* __restrict__ out,
     const float* __restrict__ lse, const uint16_t* __restrict__ dout, void* ws_base, int nslot, int nvis_cap,
-    float* __restrict__ ori_l1, int W, float* __restrict__ cmp_l1, int cmp_slots) {
-  __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
+    float* __restrict__ ori_l1, int W, float* __restrict__ cmp_l1, int cmp_slots, uint16_t* __restrict__ dq) {
+  // three kv tiles in flight: tile t is multiplied into S and dP while tile t - 1 finishes
+  // its dq product and tile t + 1 loads
+  __shared__ __attribute__((aligned(1024))) unsigned char kt[3 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char dsb[2][kNT * kDsStride];  // scale dS [key][head]
   __shared__ int32_t crow[kMaxTopk];
-  __shared__ uint32_t wsum[kWaves];
+  __shared__ uint32_t wsum[2 * kWaves];
   __shared__ float l1s[2][kWaves][kNT];  // per-wavefront head sums, added in a fixed order
 
   const int i = static_cast<int>(blockIdx.x);
   if (i >= Tq) return;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool s_wave = wave8 < kWaves;
+  const int wave = wave8 & (kWaves - 1);  // head block of this wavefront
   const int n = lane & 15, g = lane >> 4;
   const int head = 16 * wave + n;
   const bool sparse = cmp_kv != nullptr && cmp_idx != nullptr;
@@ -148,7 +158,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float scale_log2 = scale * kLog2e;
 
   int vals[NC];
-  if (sparse) {
+#pragma unroll
+  for (int ch = 0; ch < NC; ++ch) vals[ch] = -1;
+  if (sparse && s_wave) {
     const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) {
@@ -156,47 +168,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       vals[ch] = (j < topk) ? row[j] : -1;
     }
   }
-  const long long qoff = (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
-  bf16x8 qf[16], df[16];
-  load_qstyle(q + qoff, qf);
-  load_qstyle(dout + qoff, df);
-  // D = dout . out of head 16 wave + n: each lane sums its 128 dims, then the quad
-  float dsum = 0.f;
-  {
-    bf16x8 of[16];
-    load_qstyle(out + qoff, of);
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dsum += static_cast<float>(df[ks][j]) * static_cast<float>(of[ks][j]);
-  }
-  const float Dh = quad_sum(dsum);
-  const float lse2_h = lse[static_cast<long long>(i) * 64 + head] * kLog2e;
-  // The S tiles (heads x keys) give lane (n, g) the heads 16 wave + 4 g + j.
-  float lse2[4], Dq[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    lse2[j] = __shfl(lse2_h, 4 * g + j, 64);
-    Dq[j] = __shfl(Dh, 4 * g + j, 64);
-  }
 
   BwdKeys qk = bwd_ranges(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr && !sparse, Tc);
-  // compressed rows past the caller's Tc are never read (nor their gradients written)
+  // compressed rows past the caller's Tc are never read (nor their gradients written);
+  // every wavefront takes part in the compaction's barriers, the dq ones with no entries
   if (sparse) qk.ncmp = compact_rows(vals, topk, min(cu_cmp[B], Tc), crow, wsum);
   const int nkeys = min(qk.nwin + qk.ncmp, nslot);  // the workspace holds nslot keys per query
   const int ntiles = (nkeys + kNT - 1) / kNT;
   if (tid == 0) ws.nkeys[i] = nkeys;
   if (i == 0 && tid < kSlotBytes / 16) reinterpret_cast<u32x4*>(ws.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
-  if (sinks != nullptr && g == 0)
-    ws.sink_terms[static_cast<long long>(i) * 64 + head] = -exp2f(sinks[head] * kLog2e - lse2_h) * Dh;
   // Map of the visible compressed rows for the key-major dkv pass (sparse mode): the
   // compacted index of each selected row, -1 elsewhere.
   if (sparse && nvis_cap > 0) {
     int16_t* m = ws.cmap + static_cast<long long>(i) * nvis_cap;
     const int nv = min(qk.nvis, nvis_cap);
-    for (int v = tid; v < nv; v += kThreads) m[v] = -1;
+    for (int v = tid; v < nv; v += kPrepThreads) m[v] = -1;
     __syncthreads();  // the -1 fill lands before the entries below
-    for (int j = tid; j < qk.ncmp; j += kThreads) {
+    for (int j = tid; j < qk.ncmp; j += kPrepThreads) {
       const int v = crow[j] - qk.cmp_base;
       if (v >= 0 && v < nv && qk.nwin + j < nslot) m[v] = static_cast<int16_t>(j);
     }
@@ -210,9 +198,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
     return -1 - c;
   };
+  // tile t into kv buffer bf: wavefront w8 loads rows 8 pass + w8 (pass < 4)
   auto issue = [&](int t, int bf) {
-    const int p = lane & 7;
-    int kidx = t * kNT + 4 * p + wave;
+    int kidx = t * kNT + 8 * (lane & 3) + wave8;
     kidx = (kidx < nkeys) ? kidx : 0;
     const int code = key_code(kidx);
     const uint16_t* src = (code >= 0) ? ori_kv + static_cast<long long>(code) * 512
@@ -220,188 +208,176 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const unsigned long long a = reinterpret_cast<unsigned long long>(src);
     const uint32_t a_lo = static_cast<uint32_t>(a), a_hi = static_cast<uint32_t>(a >> 32);
 #pragma unroll
-    for (int pass = 0; pass < kNT / kWaves; ++pass) {
-      const int rr = pass * kWaves + wave;
+    for (int pass = 0; pass < kNT / 8; ++pass) {
+      const int rr = 8 * pass + wave8;
       const unsigned long long base = (static_cast<unsigned long long>(__builtin_amdgcn_readlane(a_hi, pass)) << 32) |
                                       static_cast<uint32_t>(__builtin_amdgcn_readlane(a_lo, pass));
       row_to_lds(reinterpret_cast<const void*>(base), lane16,
                  kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
     }
   };
-  // key rows of every slot, for the dq pass (slots past nkeys: the row of key 0)
-  for (int k = tid; k < ntiles * kNT; k += kThreads)
-    ws.codes[static_cast<long long>(i) * nslot + k] = key_code(k < nkeys ? k : 0);
   if (ntiles > 0) issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
 
-  const int offq = kpi(n) * kRowStride + 8 * g;
-  auto flush_l1 = [&](int t) {  // head-averaged probabilities of tile t
-    if (tid < kNT) {
-      const int kidx = t * kNT + tid;
-      const float (&part)[kWaves][kNT] = l1s[t & 1];
-      const float v = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) * (1.f / 64.f);
-      if (kidx < nkeys) {
-        if (kidx < qk.nwin) {
-          if (ori_l1 != nullptr && kidx < W) ori_l1[static_cast<long long>(i) * W + kidx] = v;
-        } else if (cmp_l1 != nullptr && kidx - qk.nwin < cmp_slots) {
-          cmp_l1[static_cast<long long>(i) * cmp_slots + kidx - qk.nwin] = v;
+  if (s_wave) {
+    const long long qoff = (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
+    bf16x8 qf[16], df[16];
+    load_qstyle(q + qoff, qf);
+    load_qstyle(dout + qoff, df);
+    // D = dout . out of head 16 wave + n: each lane sums its 128 dims, then the quad
+    float dsum = 0.f;
+    {
+      bf16x8 of[16];
+      load_qstyle(out + qoff, of);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dsum += static_cast<float>(df[ks][j]) * static_cast<float>(of[ks][j]);
+    }
+    const float Dh = quad_sum(dsum);
+    const float lse2_h = lse[static_cast<long long>(i) * 64 + head] * kLog2e;
+    if (sinks != nullptr && g == 0)
+      ws.sink_terms[static_cast<long long>(i) * 64 + head] = -exp2f(sinks[head] * kLog2e - lse2_h) * Dh;
+    // The S tiles (heads x keys) give lane (n, g) the heads 16 wave + 4 g + j.
+    float lse2[4], Dq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      lse2[j] = __shfl(lse2_h, 4 * g + j, 64);
+      Dq[j] = __shfl(Dh, 4 * g + j, 64);
+    }
+    const int offq = kpi(n) * kRowStride + 8 * g;
+    auto flush_l1 = [&](int t) {  // head-averaged probabilities of tile t
+      if (tid < kNT) {
+        const int kidx = t * kNT + tid;
+        const float (&part)[kWaves][kNT] = l1s[t & 1];
+        const float v = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) * (1.f / 64.f);
+        if (kidx < nkeys) {
+          if (kidx < qk.nwin) {
+            if (ori_l1 != nullptr && kidx < W) ori_l1[static_cast<long long>(i) * W + kidx] = v;
+          } else if (cmp_l1 != nullptr && kidx - qk.nwin < cmp_slots) {
+            cmp_l1[static_cast<long long>(i) * cmp_slots + kidx - qk.nwin] = v;
+          }
+        }
+      }
+    };
+    unsigned char* slot_base = ws.slots + static_cast<long long>(i) * nslot * kSlotBytes + 2 * (16 * wave + 4 * g);
+
+    for (int t = 0; t < ntiles; ++t) {
+      const int bf = t & 1;
+      // This wavefront's rows of tile t have landed and its LDS writes of tile t - 1 are
+      // done.  Vector memory operations retire in issue order and the last four issued
+      // are the slot-row stores of tile t - 1 (after the loads of tile t), so those may
+      // stay in flight: vmcnt(4), lgkmcnt(0).
+      __builtin_amdgcn_s_waitcnt(0x0074);
+      tile_barrier();  // all rows landed; kv buffer (t + 1) % 3 and dS buffer bf are free
+      if (t + 1 < ntiles) issue(t + 1, (t + 1) % 3);
+      if (want_l1 && t > 0) flush_l1(t - 1);
+      const unsigned char* tb = kt + (t % 3) * kTileBytes;
+
+      // ---- S = Q . K^T and dP = dout . K^T (heads x keys) from the same K fragments (K = V)
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const bf16x8 a0 = kfrag(tb, offq + 64 * ks, offq + 64 * ks + 32);
+        const bf16x8 a1 = kfrag(tb + 16 * kRowStride, offq + 64 * ks, offq + 64 * ks + 32);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], a0, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], a1, s1, 0, 0, 0);
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], a0, p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], a1, p1, 0, 0, 0);
+      }
+
+      // ---- lane (n, g): keys kpi(n) and 16 + kpi(n) of the tile, heads 16 wave + 4 g + j
+      const int k0 = kpi(n), k1 = 16 + kpi(n);
+      const bool v0 = t * kNT + k0 < nkeys, v1 = t * kNT + k1 < nkeys;
+      bf16x4 P0, P1, S0, S1;
+      float l0 = 0.f, l1 = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pa = v0 ? exp2f(s0[j] * scale_log2 - lse2[j]) : 0.f;
+        const float pb = v1 ? exp2f(s1[j] * scale_log2 - lse2[j]) : 0.f;
+        P0[j] = static_cast<__bf16>(pa);
+        P1[j] = static_cast<__bf16>(pb);
+        S0[j] = static_cast<__bf16>(scale * pa * (p0[j] - Dq[j]));
+        S1[j] = static_cast<__bf16>(scale * pb * (p1[j] - Dq[j]));
+        l0 += pa;
+        l1 += pb;
+      }
+      unsigned char* row0 = slot_base + static_cast<long long>(t * kNT + k0) * kSlotBytes;
+      unsigned char* row1 = slot_base + static_cast<long long>(t * kNT + k1) * kSlotBytes;
+      *reinterpret_cast<uint2*>(row0) = __builtin_bit_cast(uint2, S0);
+      *reinterpret_cast<uint2*>(row0 + 128) = __builtin_bit_cast(uint2, P0);
+      *reinterpret_cast<uint2*>(row1) = __builtin_bit_cast(uint2, S1);
+      *reinterpret_cast<uint2*>(row1 + 128) = __builtin_bit_cast(uint2, P1);
+      *reinterpret_cast<uint2*>(dsb[bf] + k0 * kDsStride + 2 * (16 * wave + 4 * g)) = __builtin_bit_cast(uint2, S0);
+      *reinterpret_cast<uint2*>(dsb[bf] + k1 * kDsStride + 2 * (16 * wave + 4 * g)) = __builtin_bit_cast(uint2, S1);
+      if (want_l1) {
+        // sum over the 16 heads of this wavefront (4 per lane, then the lane quad); the
+        // four wavefront sums meet in LDS
+        l0 = quad_sum(l0);
+        l1 = quad_sum(l1);
+        if (g == 0) {
+          l1s[bf][wave][k0] = l0;
+          l1s[bf][wave][k1] = l1;
         }
       }
     }
-  };
-  unsigned char* slot_base = ws.slots + static_cast<long long>(i) * nslot * kSlotBytes + 2 * (16 * wave + 4 * g);
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int bf = t & 1;
-    // this wavefront's rows of tile t have landed and its LDS writes of tile t - 1 are done
-    __builtin_amdgcn_s_waitcnt(0x0070);
-    tile_barrier();  // all rows landed; buffer bf ^ 1 is free; l1s[bf ^ 1] is complete
-    if (t + 1 < ntiles) issue(t + 1, bf ^ 1);
-    if (want_l1 && t > 0) flush_l1(t - 1);
-    const unsigned char* tb = kt + bf * kTileBytes;
-
-    // ---- S = Q . K^T and dP = dout . K^T (heads x keys) from the same K fragments (K = V)
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0, p0 = s0, p1 = s0;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8 a0 = kfrag(tb, offq + 64 * ks, offq + 64 * ks + 32);
-      const bf16x8 a1 = kfrag(tb + 16 * kRowStride, offq + 64 * ks, offq + 64 * ks + 32);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], a0, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[ks], a1, s1, 0, 0, 0);
-      p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], a0, p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(df[ks], a1, p1, 0, 0, 0);
+    if (ntiles > 0) {
+      lds_barrier();  // pairs with the dq wavefronts' last barrier
+      if (want_l1) flush_l1(ntiles - 1);
     }
-
-    // ---- lane (n, g): keys kpi(n) and 16 + kpi(n) of the tile, heads 16 wave + 4 g + j
-    const int k0 = kpi(n), k1 = 16 + kpi(n);
-    const bool v0 = t * kNT + k0 < nkeys, v1 = t * kNT + k1 < nkeys;
-    bf16x4 P0, P1, S0, S1;
-    float l0 = 0.f, l1 = 0.f;
+  } else {
+    // dq^T (dims x heads) += kv^T . (scale dS)^T per tile: the A operand comes from
+    // transpose reads of the kv tile (lane (n, g): dim 16 mb + n, keys kpi(4 g + j) and
+    // 16 + kpi(4 g + j)), the B operand from transpose reads of the tile's dS rows (source
+    // lane m of lane group g points at key kpi(4 g + m / 4), heads 16 wave + 4 (m % 4) ..).
+    f32x4 o[32];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float pa = v0 ? exp2f(s0[j] * scale_log2 - lse2[j]) : 0.f;
-      const float pb = v1 ? exp2f(s1[j] * scale_log2 - lse2[j]) : 0.f;
-      P0[j] = static_cast<__bf16>(pa);
-      P1[j] = static_cast<__bf16>(pb);
-      S0[j] = static_cast<__bf16>(scale * pa * (p0[j] - Dq[j]));
-      S1[j] = static_cast<__bf16>(scale * pb * (p1[j] - Dq[j]));
-      l0 += pa;
-      l1 += pb;
-    }
-    unsigned char* row0 = slot_base + static_cast<long long>(t * kNT + k0) * kSlotBytes;
-    unsigned char* row1 = slot_base + static_cast<long long>(t * kNT + k1) * kSlotBytes;
-    *reinterpret_cast<uint2*>(row0) = __builtin_bit_cast(uint2, S0);
-    *reinterpret_cast<uint2*>(row0 + 128) = __builtin_bit_cast(uint2, P0);
-    *reinterpret_cast<uint2*>(row1) = __builtin_bit_cast(uint2, S1);
-    *reinterpret_cast<uint2*>(row1 + 128) = __builtin_bit_cast(uint2, P1);
-    if (want_l1) {
-      // sum over the 16 heads of this wavefront (4 per lane, then the lane quad); the
-      // four wavefront sums meet in LDS
-      l0 = quad_sum(l0);
-      l1 = quad_sum(l1);
-      if (g == 0) {
-        l1s[bf][wave][k0] = l0;
-        l1s[bf][wave][k1] = l1;
+    for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int offv = kpi(4 * g + (n >> 2)) * kRowStride + 8 * (n & 3);
+    const int dso = kpi(4 * g + (n >> 2)) * kDsStride + 2 * (16 * wave + 4 * (n & 3));
+    auto dq_tile = [&](int t) {
+      const unsigned char* tb = kt + (t % 3) * kTileBytes;
+      const unsigned char* dsr = dsb[t & 1];
+      const bf16x4 slo = ds_read_tr(dsr + dso);
+      const bf16x4 shi = ds_read_tr(dsr + dso + 16 * kDsStride);
+      const bf16x8 sf = {slo[0], slo[1], slo[2], slo[3], shi[0], shi[1], shi[2], shi[3]};
+      bf16x4 vlo[4], vhi[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        vlo[mb] = ds_read_tr(tb + offv + 32 * mb);
+        vhi[mb] = ds_read_tr(tb + offv + 32 * mb + 16 * kRowStride);
       }
-    }
-  }
-  if (want_l1 && ntiles > 0) {
-    lds_barrier();
-    flush_l1(ntiles - 1);
-  }
-}
-
-// ----------------------------------------------------------------------------- dq
-
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_bwd_dq_kernel(
-    const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv, int Tq, const void* ws_base, int nslot,
-    int nvis_cap, uint16_t* __restrict__ dq) {
-  __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) unsigned char dsb[2][kNT * kDsStride];
-  const int i = static_cast<int>(blockIdx.x);
-  if (i >= Tq) return;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
-  const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot, nvis_cap);
-  const int nkeys = __builtin_amdgcn_readfirstlane(ws.nkeys[i]);
-  const int ntiles = (nkeys + kNT - 1) / kNT;
-  const int32_t* codes = ws.codes + static_cast<long long>(i) * nslot;
-  const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
-  const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
-  auto issue = [&](int t, int bf) {
-    const int code = codes[t * kNT + 4 * (lane & 7) + wave];
-    const uint16_t* src = (code >= 0) ? ori_kv + static_cast<long long>(code) * 512
-                                      : cmp_kv + static_cast<long long>(-1 - code) * 512;
-    const unsigned long long a = reinterpret_cast<unsigned long long>(src);
-    const uint32_t a_lo = static_cast<uint32_t>(a), a_hi = static_cast<uint32_t>(a >> 32);
 #pragma unroll
-    for (int pass = 0; pass < kNT / kWaves; ++pass) {
-      const int rr = pass * kWaves + wave;
-      const unsigned long long base = (static_cast<unsigned long long>(__builtin_amdgcn_readlane(a_hi, pass)) << 32) |
-                                      static_cast<uint32_t>(__builtin_amdgcn_readlane(a_lo, pass));
-      row_to_lds(reinterpret_cast<const void*>(base), lane16,
-                 kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
+      for (int mb = 0; mb < 32; ++mb) {
+        const int sl = mb % 4;
+        const bf16x8 av = {vlo[sl][0], vlo[sl][1], vlo[sl][2], vlo[sl][3],
+                           vhi[sl][0], vhi[sl][1], vhi[sl][2], vhi[sl][3]};
+        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sf, o[mb], 0, 0, 0);
+        if (mb + 4 < 32) {
+          vlo[sl] = ds_read_tr(tb + offv + 32 * (mb + 4));
+          vhi[sl] = ds_read_tr(tb + offv + 32 * (mb + 4) + 16 * kRowStride);
+        }
+      }
+    };
+    for (int t = 0; t < ntiles; ++t) {
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      tile_barrier();  // tile t landed; the dS rows of tile t - 1 are complete
+      if (t + 1 < ntiles) issue(t + 1, (t + 1) % 3);
+      if (t > 0) dq_tile(t - 1);
     }
-  };
-  // this thread's 16 bytes of a tile's scale * dS rows: slot tid / 8, heads 8 (tid % 8) ..
-  const unsigned char* ds_src =
-      ws.slots + (static_cast<long long>(i) * nslot + (tid >> 3)) * kSlotBytes + (tid & 7) * 16;
-  const int ds_dst = (tid >> 3) * kDsStride + (tid & 7) * 16;
-  u32x4 dreg = {0u, 0u, 0u, 0u};
-  if (ntiles > 0) {
-    issue(0, 0);
-    dreg = *reinterpret_cast<const u32x4*>(ds_src);
-  }
-  f32x4 o[32];
-#pragma unroll
-  for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int offv = kpi(4 * g + (n >> 2)) * kRowStride + 8 * (n & 3);
-  // B operand (scale dS)^T through transpose reads: source lane m of lane group g points
-  // at slot kpi(4 g + m / 4), heads 16 wave + 4 (m % 4) .., so lane (n, g) receives head
-  // 16 wave + n at keys kpi(4 g + j) (and 16 + kpi(4 g + j) from the second read).
-  const int dso = kpi(4 * g + (n >> 2)) * kDsStride + 2 * (16 * wave + 4 * (n & 3));
-  for (int t = 0; t < ntiles; ++t) {
-    const int bf = t & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // kv rows of tile t landed (dreg is waited for by the compiler)
-    *reinterpret_cast<u32x4*>(dsb[bf] + ds_dst) = dreg;
-    lds_barrier();  // dS rows of tile t visible; every wavefront is done with tile t - 1
-    if (t + 1 < ntiles) {
-      issue(t + 1, bf ^ 1);
-      dreg = *reinterpret_cast<const u32x4*>(ds_src + static_cast<long long>(t + 1) * kNT * kSlotBytes);
+    if (ntiles > 0) {
+      lds_barrier();  // the dS rows of the last tile
+      dq_tile(ntiles - 1);
     }
-    const unsigned char* tb = kt + bf * kTileBytes;
-    const bf16x4 slo = ds_read_tr(dsb[bf] + dso);
-    const bf16x4 shi = ds_read_tr(dsb[bf] + dso + 16 * kDsStride);
-    const bf16x8 sf = {slo[0], slo[1], slo[2], slo[3], shi[0], shi[1], shi[2], shi[3]};
-    bf16x4 vlo[4], vhi[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      vlo[mb] = ds_read_tr(tb + offv + 32 * mb);
-      vhi[mb] = ds_read_tr(tb + offv + 32 * mb + 16 * kRowStride);
-    }
+    // dq^T column (head 16 wave + n), dims 16 mb + 4 g + j: 8 bytes per lane and block
+    uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * wave + n) * 512 + 4 * g;
 #pragma unroll
     for (int mb = 0; mb < 32; ++mb) {
-      const int sl = mb % 4;
-      const bf16x8 a = {vlo[sl][0], vlo[sl][1], vlo[sl][2], vlo[sl][3],
-                        vhi[sl][0], vhi[sl][1], vhi[sl][2], vhi[sl][3]};
-      o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, sf, o[mb], 0, 0, 0);
-      if (mb + 4 < 32) {
-        vlo[sl] = ds_read_tr(tb + offv + 32 * (mb + 4));
-        vhi[sl] = ds_read_tr(tb + offv + 32 * (mb + 4) + 16 * kRowStride);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0])) |
+                          (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1])) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2])) |
+                          (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3])) << 16);
+      *reinterpret_cast<uint2*>(qrow + 16 * mb) = make_uint2(w0, w1);
     }
-  }
-  // dq^T column (head 16w + n), dims 16 mb + 4 g + j; rows of 8 bytes per lane
-  uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * wave + n) * 512 + 4 * g;
-#pragma unroll
-  for (int mb = 0; mb < 32; ++mb) {
-    const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0])) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1])) << 16);
-    const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2])) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3])) << 16);
-    *reinterpret_cast<uint2*>(qrow + 16 * mb) = make_uint2(w0, w1);
   }
 }
 
@@ -786,11 +762,9 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
   const auto* c16 = static_cast<const uint16_t*>(cmp_kv);
   const auto* d16 = static_cast<const uint16_t*>(dout);
   auto prep = (topk <= 2 * kThreads) ? mla_bwd_prep_kernel<2> : mla_bwd_prep_kernel<kMaxTopk / kThreads>;
-  hipLaunchKernelGGL(prep, dim3(Tq), dim3(kThreads), 0, s, q16, kv16, c16, cmp_idx, topk, Tq, Tc, cu_q, cu_kv,
+  hipLaunchKernelGGL(prep, dim3(Tq), dim3(kPrepThreads), 0, s, q16, kv16, c16, cmp_idx, topk, Tq, Tc, cu_q, cu_kv,
                      cu_cmp, B, global_start, r, wl_c, wr_c, sinks, scale, static_cast<const uint16_t*>(out), lse, d16,
-                     workspace, nslot, nvis_cap, ori_l1, W, cmp_l1, cmp_slots);
-  hipLaunchKernelGGL(mla_bwd_dq_kernel, dim3(Tq), dim3(kThreads), 0, s, kv16, c16, Tq,
-                     static_cast<const void*>(workspace), nslot, nvis_cap, static_cast<uint16_t*>(dq));
+                     workspace, nslot, nvis_cap, ori_l1, W, cmp_l1, cmp_slots, static_cast<uint16_t*>(dq));
   // dkv: an upper bound of the workgroup slots per XCD (the exact count needs cu_seqlens
   // on the host): groups <= Tq / 128 + B, each with at most n_w + n_c items x 2 halves
   const long long seg_max = max(1, max_seqlen_kv);

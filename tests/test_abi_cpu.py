@@ -129,19 +129,19 @@ def test_sparse_mla_bwd_rejects(kw, code):
 
 
 def test_sparse_mla_bwd_workspace_size_formula():
-    # per query: 32-rounded key slots x (256 B of scale*dS and P + a 4 B key row) + 4 B + 64 sink terms x 4 B,
+    # per query: 32-rounded key slots x 256 B of scale*dS and P + 4 B + 64 sink terms x 4 B,
     # plus a 2 B selection-map entry per visible compressed row in the sparse mode; then, 16-byte aligned,
     # one 256 B row of zeros
     def total(Tq, per_query):
         return (Tq * per_query + 15) // 16 * 16 + 256
     n = LIB.csa_sparse_mla_bwd_workspace_bytes(10, 127, 0, FAKE, FAKE, 512, 4096, 4)
-    assert n == total(10, 640 * (256 + 4) + 4 + 256 + 2 * 1024)
+    assert n == total(10, 640 * 256 + 4 + 256 + 2 * 1024)
     n_all = LIB.csa_sparse_mla_bwd_workspace_bytes(3, 127, 0, FAKE, None, 0, 1000, 4)  # attend-all: 128 + 250 keys
-    assert n_all == total(3, 384 * (256 + 4) + 4 + 256)
+    assert n_all == total(3, 384 * 256 + 4 + 256)
     assert LIB.csa_sparse_mla_bwd_workspace_bytes(-1, 127, 0, None, None, 0, 0, 4) == -1
     # a window wider than the longest segment holds at most max_seqlen_kv keys
     n_wide = LIB.csa_sparse_mla_bwd_workspace_bytes(2, 100000, 0, None, None, 0, 300, 4)
-    assert n_wide == total(2, 320 * (256 + 4) + 4 + 256)
+    assert n_wide == total(2, 320 * 256 + 4 + 256)
 
 
 def test_validate_layout_rejects_bad_arguments():
