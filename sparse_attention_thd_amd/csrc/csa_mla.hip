@@ -1,14 +1,18 @@
 // Sparse MLA forward: window branch + compressed branch + per-head sink over one
 // shared latent KV (keys are values), fp32 online softmax.
 //
-// MFMA path, (H, d) = (64, 512) bf16: one workgroup of 4 wavefronts per query,
-// wavefront w owning heads [16w, 16w+16).  Keys stream through LDS in tiles of 32
-// rows (window rows first, then the compacted compressed rows).  Per tile:
-//   S^T[32 keys x 16 heads] = K[32 x 512] . Q^T[512 x 16]      (A = K from LDS, B = Q in VGPRs)
-//   online softmax per head in registers (each lane owns one head column)
-//   O^T[512 x 16] += V^T[512 x 32] . P^T[32 x 16]              (A = V^T from LDS, B = P in VGPRs)
-// so the S^T accumulator layout is directly the P^T operand and every lane's
-// O^T accumulators belong to the head whose softmax state it holds.
+// MFMA path, (H, d) = (64, 512) bf16: one workgroup of 4 wavefronts per query.  Keys
+// stream through LDS in tiles of 32 rows (window rows first, then the compacted
+// compressed rows).  Per tile, wavefront w
+//   forms S^T[32 keys x 16 heads] = K[32 x 512] . Q^T[512 x 16] for heads [16w, 16w+16)
+//     (A = K from LDS, B = Q in VGPRs) and runs their online softmax in registers (each
+//     lane owns one head column); the accumulator layout of S^T is directly the P^T
+//     MFMA operand, which goes to LDS as plain 16-byte fragments with the heads'
+//     rescale factors;
+//   then, after a barrier, accumulates O^T[128 dims x 64 heads] += V^T[128 x 32] . P^T[32 x 64]
+//     for latent dims [128w, 128w+128) (A = V^T from LDS, B = the four P^T fragments).
+// Splitting the PV product by dims means each V element is read from LDS once per
+// workgroup instead of once per head block.
 //
 // Generic path (H * d <= 8192, either dtype): scalar fp32, one key at a time.
 #include "csa_common.h"
@@ -82,6 +86,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
     int wr, const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char pfr[kWaves * 64 * 16];  // P^T fragments of the tile
+  __shared__ float alpha_h[64];  // per-head rescale factor of the tile (1 when not rescaled)
+  __shared__ int resc[kWaves];   // whether head block w rescaled in this tile
   __shared__ int32_t crow[kMaxTopk];
   __shared__ uint32_t wsum[kWaves];
 
@@ -277,12 +284,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
     tmax = quad_max(tmax);
     // Lazy rescale: keep a stale maximum while the tile stays within 2^8 of it.
-    if (__any(tmax > m_run + 8.f)) {
+    const bool rescale = __any(tmax > m_run + 8.f);
+    float alpha = 1.f;
+    if (rescale) {
       const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
+      alpha = exp2f(m_run - m_new);
       l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 32; ++mb) o[mb] *= alpha;
       m_run = m_new;
     }
     bf16x8 pb;
@@ -292,60 +299,83 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       l_run += p;
       pb[j] = static_cast<__bf16>(p);
     }
+    // publish this head block's P^T fragment and rescale factors to the workgroup
+    *reinterpret_cast<bf16x8*>(pfr + (wave * 64 + lane) * 16) = pb;
+    if (g == 0) alpha_h[head] = alpha;
+    if (lane == 0) resc[wave] = rescale ? 1 : 0;
+    lds_barrier();  // every head block's P^T and factors are visible (tile t + 1 stays in flight)
 
-    // ---- O^T += V^T . P^T; k-slot 8g+j <-> key kpi(4g+j) (j < 4) or 16+kpi(4g+j-4).  The V^T
-    // fragments (two transpose reads each) are staged kVD MFMAs ahead.
-    {
-      bf16x4 vlo[kVD], vhi[kVD];
+    // ---- O^T[dims 128 wave + 16 db .. , heads 16 hb + n] += V^T . P^T.  k-slot 8g+j <->
+    // key kpi(4g+j) (j < 4) or 16+kpi(4g+j-4), in both operands.
+    if (resc[0] | resc[1] | resc[2] | resc[3]) {
 #pragma unroll
-      for (int mb = 0; mb < kVD; ++mb) {
-        const unsigned char* pv = tb + offv + 32 * mb;
-        vlo[mb] = ds_read_tr(pv);
-        vhi[mb] = ds_read_tr(pv + 16 * kRowStride);
+      for (int hb = 0; hb < 4; ++hb) {
+        const float a = alpha_h[16 * hb + n];
+#pragma unroll
+        for (int db = 0; db < 8; ++db) o[8 * hb + db] *= a;
       }
+    }
+    {
+      bf16x8 pf[4];
 #pragma unroll
-      for (int mb = 0; mb < 32; ++mb) {
-        const int sl = mb % kVD;
+      for (int hb = 0; hb < 4; ++hb) pf[hb] = *reinterpret_cast<const bf16x8*>(pfr + (hb * 64 + lane) * 16);
+      bf16x4 vlo[2], vhi[2];
+      const unsigned char* pv0 = tb + offv + 32 * (8 * wave);
+      vlo[0] = ds_read_tr(pv0);
+      vhi[0] = ds_read_tr(pv0 + 16 * kRowStride);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const int sl = db & 1;
+        if (db + 1 < 8) {
+          vlo[sl ^ 1] = ds_read_tr(pv0 + 32 * (db + 1));
+          vhi[sl ^ 1] = ds_read_tr(pv0 + 32 * (db + 1) + 16 * kRowStride);
+        }
         const bf16x8 a = {vlo[sl][0], vlo[sl][1], vlo[sl][2], vlo[sl][3],
                           vhi[sl][0], vhi[sl][1], vhi[sl][2], vhi[sl][3]};
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[mb], 0, 0, 0);
-        if (mb + kVD < 32) {
-          const unsigned char* pv = tb + offv + 32 * (mb + kVD);
-          vlo[sl] = ds_read_tr(pv);
-          vhi[sl] = ds_read_tr(pv + 16 * kRowStride);
-        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[8 * hb + db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], o[8 * hb + db], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
 
   const float l_tot = quad_sum(l_run);
-  const float inv = 1.f / l_tot;
-  // Stage this wavefront's 16 head rows through its quarter of the (now idle) tile
-  // buffers so the output leaves as one contiguous 1 KiB row per store instruction.
-  // Row n, 16-byte chunk c lives at chunk c ^ swz(n).
-  tile_barrier();  // every wavefront is done reading the last tile
-  unsigned char* stage = kt + wave * (16 * kRowBytes);
+  float* inv_h = alpha_h;  // reused: 1 / l of every head
+  tile_barrier();          // every wavefront is done with the factors of the last tile
+  if (g == 0) inv_h[head] = 1.f / l_tot;
+  lds_barrier();           // all reads of the last tile are done; inv_h is visible
+  // Stage the output through the (now idle) tile buffers so it leaves as one contiguous
+  // 1 KiB head row per store instruction.  This wavefront holds dims [128 wave, +128) of
+  // every head: head row h, 16-byte chunk c lives at chunk c ^ swz(h).
   // Lane-derived offsets are recomputed from an opaque copy of the lane id so the
   // compiler does not hoist them above the tile loop (where they would spill).
   int el;
   asm volatile("v_mov_b32 %0, %1" : "=v"(el) : "v"(lane));
   const int en = el & 15, eg = el >> 4;
 #pragma unroll
-  for (int mb = 0; mb < 32; ++mb) {
-    const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0] * inv)) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1] * inv)) << 16);
-    const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2] * inv)) |
-                        (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3] * inv)) << 16);
-    const int chunk = (2 * mb + (eg >> 1)) ^ swz(en);
-    *reinterpret_cast<uint2*>(stage + en * kRowBytes + chunk * 16 + (eg & 1) * 8) = make_uint2(w0, w1);
+  for (int hb = 0; hb < 4; ++hb) {
+    const int h = 16 * hb + en;
+    const float inv = inv_h[h];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const f32x4 v = o[8 * hb + db];
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(v[0] * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16_bits(v[1] * inv)) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(v[2] * inv)) |
+                          (static_cast<uint32_t>(f32_to_bf16_bits(v[3] * inv)) << 16);
+      // dims 128 wave + 16 db + 4 eg .. + 3: chunk 16 wave + 2 db + eg / 2, half eg % 2
+      const int chunk = (16 * wave + 2 * db + (eg >> 1)) ^ swz(h);
+      *reinterpret_cast<uint2*>(kt + h * kRowBytes + chunk * 16 + (eg & 1) * 8) = make_uint2(w0, w1);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's staging writes are done
+  lds_barrier();  // every head row is complete
   uint16_t* obase = out + (static_cast<long long>(i) * 64 + 16 * wave) * 512;
 #pragma unroll
-  for (int h = 0; h < 16; ++h) {
-    const uint4 v = *reinterpret_cast<const uint4*>(stage + h * kRowBytes + ((el ^ swz(h)) << 4));
-    *reinterpret_cast<uint4*>(obase + h * 512 + el * 8) = v;
+  for (int hh = 0; hh < 16; ++hh) {
+    const int h = 16 * wave + hh;
+    const uint4 v = *reinterpret_cast<const uint4*>(kt + h * kRowBytes + ((el ^ swz(h)) << 4));
+    *reinterpret_cast<uint4*>(obase + hh * 512 + el * 8) = v;
   }
   if (lse != nullptr && g == 0) lse[static_cast<long long>(i) * 64 + head] = m_run * kLn2 + logf(l_tot);
 }
