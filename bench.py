@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA fwd tokens/s (indexer+top-k+sparse MLA), 16k THD pack; % MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-MLA_SRC = os.path.join(ROOT, "sparse_attention_thd_amd", "csrc", "csa_mla.hip")
+# sources of the sparse-MLA forward kernel (the traffic figure is tied to their hash)
+MLA_SRCS = [os.path.join(ROOT, "sparse_attention_thd_amd", "csrc", f) for f in ("csa_mla.hip", "csa_tile.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sparse_mla_pack16k.txt")
 
 WORKLOAD_TEXT = {
@@ -40,8 +41,11 @@ WORKLOAD_TEXT = {
 }
 
 
-def _sha(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def _sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _dev(a):
@@ -290,7 +294,7 @@ def main():
         # figure only counts while the kernel source is the one it was measured on
         tr = dict(line.split(":", 1) for line in open(TRAFFIC_FILE) if ":" in line and not line.startswith("#"))
         tr = {k.strip(): v.strip() for k, v in tr.items()}
-        if tr.get("kernel_source_sha256_16") == _sha(MLA_SRC) and tr.get("workload") == args.workload:
+        if tr.get("kernel_source_sha256_16") == _sha(MLA_SRCS) and tr.get("workload") == args.workload:
             traffic = float(tr["hbm_bytes_per_launch"])
     result = {
         "metric": METRIC,
