@@ -14,7 +14,8 @@ Pages cited (by title; section names as they appear on the page):
         风险与影响.
 * [HP]  "【RFC】DeepSeek-V4 CSA/HCA 自定义算子接入与对外接口对标 torch_extension",
         sections 背景, 1. npu_lightning_indexer, 2. npu_sparse_flash_mla,
-        4. npu_sparse_flash_mla_grad, 缺失入参的用途分析（对照实验）.
+        3. npu_sparse_lightning_indexer_kl_loss_grad, 4. npu_sparse_flash_mla_grad,
+        缺失入参的用途分析（对照实验）.
 * [ML]  "feat(deepseek_v4): faithful THD context-parallel path for DS4 CSA
         (bounded activation memory)", sections What, Design, GPU verification.
 
@@ -43,6 +44,11 @@ the sink receives -sum_i p_sink * D.  The two "softmax_l1_norm" outputs are the
 attention probabilities averaged over the heads, per (query, key slot): window
 slot k is stream row lo + k (win_idx order), compressed slot j is the j-th attended
 compressed row in the order the forward lists them; unused slots hold 0.
+
+Indexer KL loss (indexer_kl_grad): KL(p^ || softmax(I)) over a query's selected
+compressed rows, p^ the main attention's head-averaged probabilities at those
+slots renormalised to sum 1; gradients through I = sum_h w relu(<q_I, k>), with
+relu'(0) = 0.
 
 "parity unpinned": ``ori_win_right > 0`` (clamped at the segment end) has no
 independent pin; every other function is pinned in ``tests/test_oracle_pins.py``.
@@ -239,6 +245,72 @@ def indexer_topk(q_I, w, k_cmp, tables, topk, queries=None):
         idx[n, :len(keep)] = cand[keep]
         sc[n, :len(keep)] = s[keep]
     return idx, sc
+
+
+def indexer_kl_grad(q_I, w, k_cmp, cmp_idx, attn_l1, tables, loss_scale, queries=None):
+    """KL loss of the indexer against the main attention, and its gradients.
+
+    [HP] 3. npu_sparse_lightning_indexer_kl_loss_grad takes the indexer's q, k and w,
+    the sparse indices and attn_softmax_l1_norm; [HP] 4. says that tensor is the
+    main attention's target distribution p (head-averaged probabilities at the
+    compressed slots, shaped like the indices), fed to this operator directly.
+    [MS] 主要改动 (TND num_seqs): the loss is a mean over the global token count, and
+    the upstream gradient scale travels with it; ``loss_scale`` carries both.
+
+    Reading (the page gives the operator's inputs only): for query i with selected
+    rows c_j (the valid entries of cmp_idx[i], in order) and targets p_j =
+    attn_l1[i, j],
+        p^_j = p_j / sum_j p_j                    (the L1 normalisation of the name)
+        I_j  = sum_h w[h] relu(u_hj),  u_hj = <q_I[i, h], k_cmp[c_j]>
+        s_j  = softmax_j(I)
+        loss_i = KL(p^ || s) = sum_j p^_j (log p^_j - log s_j)      (0 log 0 = 0)
+        G_j  = loss_scale * (s_j - p^_j)          (d loss_i / d I_j = s_j - p^_j)
+        d_w[i, h]  = sum_j G_j relu(u_hj)
+        d_q[i, h]  = sum_j G_j w[h] [u_hj > 0] k_cmp[c_j]
+        d_k[c_j]  += sum_h G_j w[h] [u_hj > 0] q_I[i, h]
+    A query with no selected row or with sum_j p_j = 0 contributes nothing.
+    Returns float64 d_q [nq, H_I, d_I], d_w [nq, H_I], d_k [len(k_cmp), d_I] and
+    loss [nq] (the unscaled KL of each query).  With ``queries`` only those rows
+    contribute (d_k is then a partial sum).
+    """
+    Tq = len(tables["q_seg"])
+    qs = range(Tq) if queries is None else list(queries)
+    nq = len(qs)
+    H, dI = np.asarray(q_I[0]).shape if Tq else (0, 0)
+    kk = np.asarray(k_cmp, dtype=np.float64)
+    d_q = np.zeros((nq, H, dI), dtype=np.float64)
+    d_w = np.zeros((nq, H), dtype=np.float64)
+    d_k = np.zeros((len(kk), dI), dtype=np.float64)
+    loss = np.zeros(nq, dtype=np.float64)
+    for n, i in enumerate(qs):
+        row = np.asarray(cmp_idx[i]).reshape(-1)
+        rows = [int(c) for c in row if 0 <= int(c) < len(kk)]
+        if not rows:
+            continue
+        p = np.asarray(attn_l1[i], dtype=np.float64).reshape(-1)[:len(rows)]
+        psum = p.sum()
+        if psum <= 0.0:
+            continue
+        ph = p / psum
+        qi = np.asarray(q_I[i], dtype=np.float64)          # [H, dI]
+        wi = np.asarray(w[i], dtype=np.float64)            # [H]
+        K = kk[rows]                                       # [n, dI]
+        u = qi @ K.T                                       # [H, n]
+        I = wi @ np.maximum(u, 0.0)                        # [n]
+        z = I - I.max()
+        ls = z - math.log(np.exp(z).sum())                 # log softmax
+        sm = np.exp(ls)
+        nz = ph > 0
+        loss[n] = float((ph[nz] * (np.log(ph[nz]) - ls[nz])).sum())
+        G = loss_scale * (sm - ph)                         # [n]
+        act = (u > 0.0).astype(np.float64)                 # [H, n]
+        d_w[n] = np.maximum(u, 0.0) @ G
+        coef = wi[:, None] * act * G[None, :]              # [H, n]
+        d_q[n] = coef @ K
+        contrib = coef.T @ qi                              # [n, dI]
+        for j, c in enumerate(rows):
+            d_k[c] += contrib[j]
+    return dict(d_q=d_q, d_w=d_w, d_k=d_k, loss=loss)
 
 
 # --------------------------------------------------------------------------- sparse MLA
