@@ -233,6 +233,45 @@ int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, co
                        void* workspace, int64_t workspace_bytes, csa_stream_t stream);
 
 /*
+ * csa_indexer_kl_grad - the lightning indexer's KL loss against the main attention and
+ * its gradients ([HP] 3. npu_sparse_lightning_indexer_kl_loss_grad: inputs q, k, w,
+ * the sparse indices and attn_softmax_l1_norm; [HP] 4.: that tensor is the main
+ * attention's target distribution, i.e. the cmp_l1 output of csa_sparse_mla_bwd).
+ *
+ * For local query i with selected compressed rows c_j (the valid entries of
+ * cmp_idx[i], in order) and targets p_j = attn_l1[i, j]:
+ *   p^ = p / sum_j p_j,  u_hj = <q_I[i,h], k_I_cmp[c_j]>,  I_j = sum_h w[i,h] relu(u_hj),
+ *   loss[i] = KL(p^ || softmax(I)),  G_j = loss_scale * (softmax_j(I) - p^_j),
+ *   d_w[i,h] = sum_j G_j relu(u_hj),   d_q_I[i,h] = sum_j G_j w[i,h] [u_hj > 0] k_I_cmp[c_j],
+ *   d_k_I_cmp[c_j] += sum_h G_j w[i,h] [u_hj > 0] q_I[i,h].
+ * loss_scale carries the upstream gradient and the mean over the global token count
+ * ([MS] 主要改动: in TND the loss divides by the global token count).  A query with
+ * nothing selected or zero target mass contributes nothing (loss 0).  Scores are
+ * float32 MFMA sums of the bf16 inputs; M = G w [u > 0] enters the d_q / d_k
+ * products as bf16.
+ *   q_I [Tq, H_I, d_I], w [Tq, H_I], k_I_cmp [Tc, d_I] (call dtype), cmp_idx [Tq, topk]
+ *   int32 whose valid entries are distinct rows visible to the query (what
+ *   csa_indexer_topk emits), attn_l1 [Tq, topk] float32 (slot j = the j-th valid
+ *   entry), d_q_I [Tq, H_I, d_I] (call dtype), d_w [Tq, H_I] float32, d_k_I_cmp
+ *   [Tc, d_I] float32 (overwritten), loss [Tq] float32 (NULL = not written: the
+ *   unscaled KL of each query).
+ * workspace: at least csa_indexer_kl_grad_workspace_bytes() bytes (the G of every
+ * selected slot and a map of the visible rows), owned by the caller.  d_k_I_cmp takes
+ * float atomics from the query chunks that share a row tile, so its last bits vary
+ * between runs; the other outputs are deterministic.
+ * Errors: EINVAL for NULL pointers, topk < 1, B < 1, Tq < 0, Tc < 0, cmp_ratio < 1,
+ * global_start < 0, max_seqlen_kv < 0 or a workspace smaller than required;
+ * EUNSUPPORTED for topk > 2048 or any shape other than (H_I, d_I) = (64, 128) bf16.
+ */
+int64_t csa_indexer_kl_grad_workspace_bytes(int32_t Tq, int32_t topk, int32_t max_seqlen_kv, int32_t cmp_ratio);
+int csa_indexer_kl_grad(const void* q_I, const void* w, const void* k_I_cmp, const int32_t* cmp_idx,
+                        const float* attn_l1, int32_t topk, int32_t Tq, int32_t Tc, int32_t H_I, int32_t d_I,
+                        int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                        const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
+                        int32_t max_seqlen_kv, float loss_scale, void* d_q_I, float* d_w, float* d_k_I_cmp,
+                        float* loss, void* workspace, int64_t workspace_bytes, csa_stream_t stream);
+
+/*
  * csa_validate_layout - synchronous debug check of a THD layout held in device
  * memory: cu_seqlens_kv starts at 0, is non-decreasing and ends at Tkv;
  * cu_seqlens_q equals clamp(cu_seqlens_kv - global_start, 0, Tq); and the longest

@@ -33,9 +33,13 @@ SIGNATURES = {
     "csa_sparse_mla_bwd_workspace_bytes": [_I, _I, _I, _P, _P, _I, _I, _I],
     "csa_sparse_mla_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                            C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, C.c_int64, _P],
+    "csa_indexer_kl_grad_workspace_bytes": [_I, _I, _I, _I],
+    "csa_indexer_kl_grad": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, C.c_float,
+                            _P, _P, _P, _P, _P, C.c_int64, _P],
     "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _P],
 }
-RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64}
+RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64,
+            "csa_indexer_kl_grad_workspace_bytes": C.c_int64}
 
 
 class CsaError(RuntimeError):
@@ -46,7 +50,7 @@ class CsaError(RuntimeError):
 
 def _load() -> C.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m sparse_attention_thd_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_attention_thd_amd/build.py`")
     lib = C.CDLL(LIB_PATH)
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -173,6 +177,28 @@ def csa_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_s
         _ptr(d_cmp_kv, "d_cmp_kv", f32, True), _ptr(d_sinks, "d_sinks", f32, True), _ptr(ori_l1, "ori_l1", f32, True),
         _ptr(cmp_l1, "cmp_l1", f32, True), cmp_slots, _ptr(workspace, "workspace", optional=True), ws_bytes,
         _stream(stream)))
+
+
+def csa_indexer_kl_grad_workspace_bytes(Tq, topk, max_seqlen_kv, cmp_ratio):
+    n = LIB.csa_indexer_kl_grad_workspace_bytes(Tq, topk, max_seqlen_kv, cmp_ratio)
+    if n < 0:
+        raise CsaError(CSA_EINVAL, "csa_indexer_kl_grad_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def csa_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, H_I, d_I, cu_seqlens_q, cu_seqlens_kv,
+                        cu_seqlens_cmp, B, global_start, cmp_ratio, max_seqlen_kv, loss_scale, d_q_I, d_w,
+                        d_k_I_cmp, loss=None, workspace=None, stream=None):
+    i32, f32 = torch.int32, torch.float32
+    dt = q_I.dtype
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(LIB.csa_indexer_kl_grad(
+        _ptr(q_I, "q_I"), _ptr(w, "w", dt), _ptr(k_I_cmp, "k_I_cmp", dt, True), _ptr(cmp_idx, "cmp_idx", i32),
+        _ptr(attn_l1, "attn_l1", f32), topk, Tq, Tc, H_I, d_I, _dtype_code(q_I),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, global_start, cmp_ratio, max_seqlen_kv, float(loss_scale),
+        _ptr(d_q_I, "d_q_I", dt), _ptr(d_w, "d_w", f32), _ptr(d_k_I_cmp, "d_k_I_cmp", f32, True),
+        _ptr(loss, "loss", f32, True), _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
 
 
 def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, stream=None):

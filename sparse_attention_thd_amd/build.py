@@ -1,6 +1,6 @@
 """Build libcsa.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m sparse_attention_thd_amd.build        # or build() from Python
+    python sparse_attention_thd_amd/build.py        # or build() from Python (__graft_entry__.build)
 
 Compiles every ``csrc/*.hip`` to an object file in ``_build/`` and links
 ``sparse_attention_thd_amd/libcsa.so``.  Always recompiles (a full build takes

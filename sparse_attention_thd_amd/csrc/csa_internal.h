@@ -33,6 +33,14 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
                                  float* d_sinks, float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap,
                                  int nvis_cap, void* workspace, hipStream_t s);
 
+hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_cmp, const int32_t* cmp_idx,
+                                  const float* attn_l1, int topk, int Tq, int Tc, const int32_t* cu_q,
+                                  const int32_t* cu_kv, const int32_t* cu_cmp, int B, int global_start, int r,
+                                  int max_seqlen_kv, float loss_scale, void* d_q, float* d_w, float* d_k, float* loss,
+                                  int nvis_cap, void* workspace, hipStream_t s);
+bool kl_shape_supported(int H_I, int d_I, int dtype);
+size_t kl_workspace_bytes(int Tq, int topk, int nvis_cap);
+
 bool indexer_shape_supported(int H_I, int d_I, int dtype);
 bool mla_shape_supported(int H, int d, int dtype);
 bool mla_bwd_shape_supported(int H, int d, int dtype);

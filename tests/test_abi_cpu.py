@@ -144,6 +144,33 @@ def test_sparse_mla_bwd_workspace_size_formula():
     assert n_wide == total(2, 320 * 256 + 4 + 256)
 
 
+def _kl(**kw):
+    a = dict(q=FAKE, w=FAKE, k=FAKE, cidx=FAKE, p=FAKE, topk=512, Tq=8, Tc=2, H=64, d=128, dtype=1, cu_q=FAKE,
+             cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, maxlen=8, scale=1.0, dq=FAKE, dw=FAKE, dk=FAKE, loss=None,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return LIB.csa_indexer_kl_grad(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), EINVAL), (dict(w=None), EINVAL), (dict(cidx=None), EINVAL), (dict(p=None), EINVAL),
+    (dict(dq=None), EINVAL), (dict(dw=None), EINVAL), (dict(dk=None), EINVAL), (dict(k=None), EINVAL),
+    (dict(ws=None), EINVAL), (dict(cu_cmp=None), EINVAL), (dict(topk=0), EINVAL), (dict(B=0), EINVAL),
+    (dict(r=0), EINVAL), (dict(gs=-1), EINVAL), (dict(ws_bytes=16), EINVAL), (dict(topk=4096), EUNSUP),
+    (dict(H=16), EUNSUP), (dict(d=64), EUNSUP), (dict(dtype=0), EUNSUP),
+])
+def test_indexer_kl_grad_rejects(kw, code):
+    assert _kl(**kw) == code
+
+
+def test_indexer_kl_grad_workspace_size_formula():
+    # per query: topk float32 slot gradients + a 2 B map entry per visible compressed row
+    assert LIB.csa_indexer_kl_grad_workspace_bytes(10, 512, 4096, 4) == 10 * (512 * 4 + 2 * 1024)
+    assert LIB.csa_indexer_kl_grad_workspace_bytes(3, 16, 1000, 128) == 3 * (16 * 4 + 2 * 7)
+    assert LIB.csa_indexer_kl_grad_workspace_bytes(-1, 16, 10, 4) == -1
+    assert LIB.csa_indexer_kl_grad_workspace_bytes(2, 0, 10, 4) == -1
+
+
 def test_validate_layout_rejects_bad_arguments():
     assert LIB.csa_validate_layout(None, FAKE, 1, 0, 0, 0, -1, None) == EINVAL
     assert LIB.csa_validate_layout(FAKE, FAKE, 0, 0, 0, 0, -1, None) == EINVAL
