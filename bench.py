@@ -2,13 +2,14 @@
 kernel's roofline fraction and the CPU oracle as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload pack16k] [--seed 0] [--no-cpu-baseline]
-                    [--no-backward] [--bwd-steps K]
+                    [--no-backward] [--bwd-steps K] [--no-kl]
 
 A step is one whole forward over the 16384-token THD pack with every input
 already resident in HBM: segment indices, compression of the latent KV and of
 the indexer keys, lightning indexer + top-k, sparse MLA.  Prints one JSON line.
-After the timed forward steps, a "backward" object times the sparse-MLA backward on
-the same pack (outside the forward's timed region).
+After the timed forward steps, a "backward" object times the sparse-MLA backward and
+an "indexer_kl" object the indexer's KL-loss gradient on the same pack (both outside
+the forward's timed region).
 """
 from __future__ import annotations
 
@@ -194,6 +195,46 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
             "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes}
 
 
+def kl_bench(plan, pack, inputs, ncmp, steps, warmup):
+    """csa_indexer_kl_grad on the forward's top-k lists with seeded targets at the kept slots.
+
+    Algorithmic work: three products of 64 heads x 128 dims per kept (query, row) pair
+    (the scores u, d_q and d_k), 6 H_I d_I flops; the kernels recompute u twice more."""
+    import torch
+    from sparse_attention_thd_amd import _lib
+    L = plan.L
+    idx = plan.topk_idx
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4321)
+    p = torch.rand(idx.shape, generator=gen, device="cuda") * (idx >= 0)
+    Tc = plan.k_I_cmp.shape[0]
+    nbytes = _lib.csa_indexer_kl_grad_workspace_bytes(L.Tq, plan.topk, L.max_seqlen_kv, plan.r)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    d_q = torch.empty_like(inputs["q_I"])
+    d_w = torch.empty((L.Tq, plan.H_I), dtype=torch.float32, device="cuda")
+    d_k = torch.empty((Tc, plan.d_I), dtype=torch.float32, device="cuda")
+    loss = torch.empty(L.Tq, dtype=torch.float32, device="cuda")
+
+    def kl():
+        _lib.csa_indexer_kl_grad(inputs["q_I"], inputs["w"], plan.k_I_cmp, idx, p, plan.topk, L.Tq, Tc, plan.H_I,
+                                 plan.d_I, L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start,
+                                 plan.r, L.max_seqlen_kv, 1.0 / L.Tq, d_q, d_w, d_k, loss, ws)
+
+    for _ in range(warmup):
+        kl()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record(); kl(); e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    flops = 6.0 * plan.H_I * plan.d_I * ncmp
+    return {"call": "csa_indexer_kl_grad (d_q_I, d_w, d_k_I_cmp, per-query KL loss)", "steps": steps,
+            "avg_call_ms": ms, "tokens_per_s": pack.Tq / (ms / 1e3), "kept_pairs": ncmp,
+            "algorithmic_flops_per_call": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12,
+            "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +246,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-backward", action="store_true", help="skip the sparse-MLA backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=10)
+    ap.add_argument("--no-kl", action="store_true", help="skip the indexer KL-loss gradient measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -324,6 +366,8 @@ def main():
     }
     if not args.no_backward and pack.H == 64 and pack.d == 512:
         result["backward"] = backward_bench(plan, pack, inputs, nwin, ncmp, args.bwd_steps, 2)
+    if not args.no_kl and plan.topk_idx is not None and pack.H_I == 64 and pack.d_I == 128:
+        result["indexer_kl"] = kl_bench(plan, pack, inputs, ncmp, args.bwd_steps, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pack, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -9,6 +9,6 @@ path (no kernels, headers, helpers, tables or rounding routines).
 from .csa_oracle import (  # noqa: F401
     NO_COMPRESS, COMPRESSOR_ONLY, INDEXER,
     layer_compress_mode, segment_table, query_table, build_indices,
-    compress, round_to_bf16, round_to_f32, round_to,
+    compress, compress_learned, round_to_bf16, round_to_f32, round_to,
     indexer_scores, indexer_topk, indexer_kl_grad, sparse_mla_fwd, sparse_mla_bwd, csa_forward,
 )

@@ -199,6 +199,61 @@ def compress(x, cu_seqlens_kv, cmp_ratio):
     return np.stack(rows)
 
 
+def compress_learned(x, wkv, wgate, ape, cu_seqlens_kv, cmp_ratio, overlap):
+    """Learned gated compressor (the alternative to mean pooling), float64.
+
+    [MI] 关键源码片段 compressor.py (_forward_thd and _overlap_transform_thd), in
+    the page's order:
+      1. two projections of the hidden rows, kv = x wkv^T and score = x wgate^T
+         (linear_bf16_fp32: bf16 operands, float32 results; here float64);
+      2. the rows of compressed row j of segment b are stream rows
+         cu_seqlens[b] + j r + m, m in [0, r) (the len % r tail forms no row);
+      3. the learned position table ape [r, C] is added to the scores by in-group
+         position m (the page prints only ``ape.view(1, ratio, 1, -1)``; the
+         reading is an addition, before the overlap step);
+      4. with overlap (C = 2 hd) the group becomes 2r positions of hd channels:
+         positions [0, r) hold the previous group's first-half channels [0, hd),
+         positions [r, 2r) the group's own second-half channels [hd, 2 hd); a
+         segment's first group has no predecessor and takes kv = 0, score = -inf
+         there.  Without overlap (C = hd) the r positions are used as they are;
+      5. the tail is elided on the page; the reading is a softmax of the scores
+         over the positions, per channel, and the softmax-weighted sum of kv.
+    x [Tkv, D]; wkv, wgate [C, D]; ape [r, C].  Returns float64 [Tc, hd].
+    """
+    cu = [int(v) for v in cu_seqlens_kv]
+    r = int(cmp_ratio)
+    kv = np.asarray(x, dtype=np.float64) @ np.asarray(wkv, dtype=np.float64).T       # step 1
+    score = np.asarray(x, dtype=np.float64) @ np.asarray(wgate, dtype=np.float64).T
+    ape = np.asarray(ape, dtype=np.float64)
+    C = kv.shape[1]
+    hd = C // 2 if overlap else C
+    out = []
+    for b in range(len(cu) - 1):
+        s, e = cu[b], cu[b + 1]
+        n = (e - s) // r
+        g_kv = [kv[s + j * r: s + j * r + r] for j in range(n)]                      # step 2
+        g_sc = [score[s + j * r: s + j * r + r] + ape for j in range(n)]             # step 3
+        for j in range(n):
+            if overlap:                                                               # step 4
+                if j == 0:
+                    prev_kv = np.zeros((r, hd))
+                    prev_sc = np.full((r, hd), -np.inf)
+                else:
+                    prev_kv = g_kv[j - 1][:, :hd]
+                    prev_sc = g_sc[j - 1][:, :hd]
+                kvw = np.concatenate([prev_kv, g_kv[j][:, hd:]], axis=0)             # [2r, hd]
+                scw = np.concatenate([prev_sc, g_sc[j][:, hd:]], axis=0)
+            else:
+                kvw, scw = g_kv[j], g_sc[j]
+            m = scw.max(axis=0)                                                       # step 5
+            p = np.exp(scw - m)
+            p = p / p.sum(axis=0)
+            out.append((p * kvw).sum(axis=0))
+    if not out:
+        return np.zeros((0, hd), dtype=np.float64)
+    return np.stack(out)
+
+
 # --------------------------------------------------------------------------- indexer
 
 def indexer_scores(q_I_i, w_i, k_rows):
