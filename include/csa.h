@@ -120,6 +120,35 @@ int csa_compress(const void* x, int32_t Tkv, int32_t d, int32_t dtype,
                  int32_t cmp_ratio, void* x_cmp, int32_t Tc_cap, csa_stream_t stream);
 
 /*
+ * csa_compress_learned - the learned gated, overlapping compressor ([MI] 关键源码片段
+ * compressor.py: _forward_thd and _overlap_transform_thd), in place of mean pooling.
+ *
+ * For compressed row c (segment b, group j = c - cu_seqlens_cmp[b], stream rows
+ * t_m = s_b + j*r + m, m < r):
+ *   kv[m]    = x[t_m] wkv^T,  score[m] = x[t_m] wgate^T + ape[m]   (C channels each)
+ *   overlap = 1 (C = 2 hd): 2r positions of hd channels, positions m < r taking the
+ *     previous group's channels [0, hd) (its kv, its score), positions r + m the
+ *     group's own channels [hd, 2 hd); a segment's first group has no previous group
+ *     (kv 0, score -inf at those positions).  overlap = 0 (C = hd): the r positions.
+ *   x_cmp[c, ch] = sum over positions of softmax(score[., ch]) kv[., ch]
+ * The page prints the position table as ape.view(1, ratio, 1, -1) without its use;
+ * it is read as an addition to the scores.  The page also elides the pooling tail;
+ * it is read as the per-channel softmax over the positions and the weighted sum.
+ * Products are bf16 x bf16 summed in float32 (MFMA), the softmax is float32 and
+ * x_cmp is rounded once to bf16.  Tail rows are never read.
+ *   x [Tkv, D], wkv and wgate [C, D] (call dtype), ape [cmp_ratio, C] float32,
+ *   x_cmp [Tc_cap, hd] (call dtype; rows >= cu_seqlens_cmp[B] untouched).
+ * Errors: EINVAL for NULL pointers, B < 1, Tkv < 0, D < 1, hd < 1, cmp_ratio < 1,
+ * overlap other than 0 / 1, Tc_cap < Tkv / r, unknown dtype; EUNSUPPORTED unless
+ * dtype is bf16, cmp_ratio = 4, D is a multiple of 64, hd a multiple of 64 (overlap)
+ * or 128 (no overlap), and x spans less than 4 GiB.
+ */
+int csa_compress_learned(const void* x, int32_t Tkv, int32_t D, int32_t dtype, const void* wkv, const void* wgate,
+                         const float* ape, int32_t hd, int32_t overlap, const int32_t* cu_seqlens_kv,
+                         const int32_t* cu_seqlens_cmp, int32_t B, int32_t cmp_ratio, void* x_cmp, int32_t Tc_cap,
+                         csa_stream_t stream);
+
+/*
  * csa_indexer_topk - lightning indexer scores and per-query top-k within the
  * query's own segment ([HP] 1. npu_lightning_indexer; [MI] 功能与动机 item 4).
  *

@@ -27,6 +27,7 @@ SIGNATURES = {
     "csa_last_error": [],
     "csa_build_indices": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P],
     "csa_compress": [_P, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P],
+    "csa_compress_learned": [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _P],
     "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
     "csa_sparse_mla_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P,
                            C.c_float, _P, _P, _P],
@@ -123,6 +124,16 @@ def csa_compress(x, Tkv, d, cu_seqlens_kv, cu_seqlens_cmp, B, cmp_ratio, x_cmp, 
     _check(LIB.csa_compress(_ptr(x, "x"), Tkv, d, _dtype_code(x), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
                             _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, cmp_ratio,
                             _ptr(x_cmp, "x_cmp", x.dtype), Tc_cap, _stream(stream)))
+
+
+def csa_compress_learned(x, Tkv, D, wkv, wgate, ape, hd, overlap, cu_seqlens_kv, cu_seqlens_cmp, B, cmp_ratio,
+                         x_cmp, Tc_cap, stream=None):
+    i32 = torch.int32
+    _check(LIB.csa_compress_learned(_ptr(x, "x"), Tkv, D, _dtype_code(x), _ptr(wkv, "wkv", x.dtype),
+                                    _ptr(wgate, "wgate", x.dtype), _ptr(ape, "ape", torch.float32), hd,
+                                    1 if overlap else 0, _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
+                                    _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, cmp_ratio,
+                                    _ptr(x_cmp, "x_cmp", x.dtype), Tc_cap, _stream(stream)))
 
 
 def csa_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,

@@ -84,6 +84,29 @@ int csa_compress(const void* x, int32_t Tkv, int32_t d, int32_t dtype, const int
                     "csa_compress");
 }
 
+int csa_compress_learned(const void* x, int32_t Tkv, int32_t D, int32_t dtype, const void* wkv, const void* wgate,
+                         const float* ape, int32_t hd, int32_t overlap, const int32_t* cu_seqlens_kv,
+                         const int32_t* cu_seqlens_cmp, int32_t B, int32_t cmp_ratio, void* x_cmp, int32_t Tc_cap,
+                         csa_stream_t stream) {
+  if (!cu_seqlens_kv || !cu_seqlens_cmp || (Tkv > 0 && (!x || !wkv || !wgate || !ape)) || (!x_cmp && Tc_cap > 0))
+    return fail(CSA_EINVAL, "csa_compress_learned: NULL pointer");
+  if (B < 1 || Tkv < 0 || D < 1 || hd < 1 || cmp_ratio < 1 || (overlap != 0 && overlap != 1))
+    return fail(CSA_EINVAL, "csa_compress_learned: need B >= 1, Tkv >= 0, D >= 1, hd >= 1, cmp_ratio >= 1, "
+                "overlap 0 or 1");
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_compress_learned: unknown dtype %d", dtype);
+  if (Tc_cap < Tkv / cmp_ratio)
+    return fail(CSA_EINVAL, "csa_compress_learned: Tc_cap (%d) < Tkv / cmp_ratio (%d)", Tc_cap, Tkv / cmp_ratio);
+  if (!csa::learned_shape_supported(D, hd, cmp_ratio, overlap, dtype))
+    return fail(CSA_EUNSUPPORTED, "csa_compress_learned: no kernel for D=%d hd=%d cmp_ratio=%d overlap=%d dtype=%d",
+                D, hd, cmp_ratio, overlap, dtype);
+  if (static_cast<long long>(Tkv) * D * 2 > 0xFFFFFFFFLL)
+    return fail(CSA_EUNSUPPORTED, "csa_compress_learned: x of %lld bytes exceeds 4 GiB",
+                static_cast<long long>(Tkv) * D * 2);
+  return hip_status(csa::launch_compress_learned(x, Tkv, D, wkv, wgate, ape, hd, overlap, cu_seqlens_kv,
+                                                 cu_seqlens_cmp, B, x_cmp, Tc_cap, static_cast<hipStream_t>(stream)),
+                    "csa_compress_learned");
+}
+
 int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_t Tq, int32_t H_I, int32_t d_I,
                      int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                      const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,

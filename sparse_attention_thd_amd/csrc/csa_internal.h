@@ -41,6 +41,11 @@ hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_
 bool kl_shape_supported(int H_I, int d_I, int dtype);
 size_t kl_workspace_bytes(int Tq, int topk, int nvis_cap);
 
+hipError_t launch_compress_learned(const void* x, int Tkv, int D, const void* wkv, const void* wgate,
+                                   const float* ape, int hd, int overlap, const int32_t* cu_kv,
+                                   const int32_t* cu_cmp, int B, void* out, int Tc_cap, hipStream_t s);
+bool learned_shape_supported(int D, int hd, int cmp_ratio, int overlap, int dtype);
+
 bool indexer_shape_supported(int H_I, int d_I, int dtype);
 bool mla_shape_supported(int H, int d, int dtype);
 bool mla_bwd_shape_supported(int H, int d, int dtype);

@@ -22,6 +22,13 @@ a 128-token window, top-512):
                 (lognormal(9,0.8) lengths): local queries are stream rows
                 [65536, 98304), KV is the prefix [0, 98304).
 * ``stress``    single4k's shape with q and kv ~ N(0,1): peaky softmax.
+
+Learned-compressor inputs (``compressor_inputs``, its own stream
+``default_rng([seed, 7])``, drawn x, wkv, wgate, ape in that order): hidden rows
+x [Tkv, D] ~ N(0,1), projections wkv, wgate [C, D] ~ N(0,1)/sqrt(D) (wgate times
+``gate_scale``), C = 2 hd with overlap else hd, and the position table
+ape [r, C] ~ N(0,1) * ``ape_scale`` in float32.  The pages do not give the model's
+hidden size; D = 4096 is this workload's choice.
 """
 from __future__ import annotations
 
@@ -237,6 +244,28 @@ CONFIGS = {
     "cp32k": _cp32k,
     "stress": _stress,
 }
+
+
+@dataclasses.dataclass
+class CompressorInputs:
+    x: np.ndarray        # [Tkv, D] bf16 bits
+    wkv: np.ndarray      # [C, D] bf16 bits
+    wgate: np.ndarray    # [C, D] bf16 bits
+    ape: np.ndarray      # [r, C] float32
+    D: int
+    hd: int
+    overlap: bool
+    cmp_ratio: int
+
+
+def compressor_inputs(Tkv, *, D=4096, hd=512, overlap=True, cmp_ratio=4, seed=0, gate_scale=1.0, ape_scale=1.0):
+    rng = np.random.default_rng([seed, 7])
+    C = 2 * hd if overlap else hd
+    x = _draw(rng, (Tkv, D), 1.0, True)
+    wkv = _draw(rng, (C, D), 1.0 / math.sqrt(D), True)
+    wgate = _draw(rng, (C, D), gate_scale / math.sqrt(D), True)
+    ape = rng.standard_normal((cmp_ratio, C), dtype=np.float32) * np.float32(ape_scale)
+    return CompressorInputs(x=x, wkv=wkv, wgate=wgate, ape=ape, D=D, hd=hd, overlap=overlap, cmp_ratio=cmp_ratio)
 
 
 def make_pack(name: str, seed: int = 0) -> Pack:

@@ -75,6 +75,30 @@ def test_compress_rejects(kw, code):
     assert _cmp(**kw) == code
 
 
+def _learned(**kw):
+    a = dict(x=FAKE, Tkv=16, D=4096, dtype=1, wkv=FAKE, wgate=FAKE, ape=FAKE, hd=512, overlap=1, cu_kv=FAKE,
+             cu_cmp=FAKE, B=1, r=4, out=FAKE, Tc_cap=4, stream=None)
+    a.update(kw)
+    return LIB.csa_compress_learned(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), EINVAL), (dict(wkv=None), EINVAL), (dict(wgate=None), EINVAL), (dict(ape=None), EINVAL),
+    (dict(out=None), EINVAL), (dict(cu_cmp=None), EINVAL), (dict(B=0), EINVAL), (dict(D=0), EINVAL),
+    (dict(hd=0), EINVAL), (dict(r=0), EINVAL), (dict(overlap=2), EINVAL), (dict(dtype=7), EINVAL),
+    (dict(Tc_cap=3), EINVAL), (dict(r=8, Tc_cap=2), EUNSUP), (dict(D=4000), EUNSUP), (dict(hd=96), EUNSUP),
+    (dict(hd=64, overlap=0), EUNSUP), (dict(dtype=0), EUNSUP), (dict(Tkv=1 << 20, Tc_cap=1 << 18), EUNSUP),
+])
+def test_compress_learned_rejects(kw, code):
+    assert _learned(**kw) == code
+
+
+def test_compress_learned_accepts_empty_streams():
+    # nothing to launch: no row reaches a complete group, or no rows at all
+    assert _learned(Tkv=0, Tc_cap=0, x=None, out=None) == 0
+    assert _learned(x=None, wkv=None, wgate=None, ape=None, Tkv=0, Tc_cap=0, out=None) == 0
+
+
 def _idx(**kw):
     a = dict(q=FAKE, w=FAKE, k=FAKE, Tq=8, H_I=64, d_I=128, dtype=1, cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE, B=1,
              gs=0, r=4, maxlen=8, topk=512, idx=FAKE, sc=None, stream=None)
