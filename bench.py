@@ -2,14 +2,15 @@
 kernel's roofline fraction and the CPU oracle as a reported baseline.
 
     python bench.py [--steps K] [--warmup W] [--workload pack16k] [--seed 0] [--no-cpu-baseline]
-                    [--no-backward] [--bwd-steps K] [--no-kl]
+                    [--no-backward] [--bwd-steps K] [--no-kl] [--no-learned]
 
 A step is one whole forward over the 16384-token THD pack with every input
 already resident in HBM: segment indices, compression of the latent KV and of
 the indexer keys, lightning indexer + top-k, sparse MLA.  Prints one JSON line.
 After the timed forward steps, a "backward" object times the sparse-MLA backward and
-an "indexer_kl" object the indexer's KL-loss gradient on the same pack (both outside
-the forward's timed region).
+an "indexer_kl" object the indexer's KL-loss gradient, and a "learned_compressor"
+object the learned gated compressor (hidden size 4096) for the latent and the indexer
+keys, all on the same pack and outside the forward's timed region.
 """
 from __future__ import annotations
 
@@ -235,6 +236,45 @@ def kl_bench(plan, pack, inputs, ncmp, steps, warmup):
             "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes}
 
 
+def learned_bench(plan, pack, steps, warmup, D=4096):
+    """csa_compress_learned on the pack's layout with seeded hidden rows and weights.
+
+    Algorithmic work: the two projections of every grouped row (Tc * r rows, 2 C
+    columns, C = 2 hd with overlap, hidden size D), 2 * rows * 2C * D flops; the
+    pooling epilogue is O(rows * C)."""
+    import torch
+    from synth import compressor_inputs
+    from sparse_attention_thd_amd import _lib
+    L = plan.L
+    Tc = int(plan.cu_seqlens_cmp[-1].item())
+    res = {}
+    for name, hd in (("latent_hd512", 512), ("indexer_hd128", 128)):
+        ci = compressor_inputs(L.Tkv, D=D, hd=hd, overlap=True, seed=21)
+        x, wkv, wgate, ape = _dev(ci.x), _dev(ci.wkv), _dev(ci.wgate), _dev(ci.ape)
+        out = torch.empty((plan.Tc_cap, hd), dtype=torch.bfloat16, device="cuda")
+
+        def run():
+            _lib.csa_compress_learned(x, L.Tkv, D, wkv, wgate, ape, hd, True, L.cu_seqlens_kv, plan.cu_seqlens_cmp,
+                                      L.B, plan.r, out, plan.Tc_cap)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in ev:
+            e0.record(); run(); e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        flops = 2.0 * (Tc * plan.r) * (2 * 2 * hd) * D
+        res[name] = {"avg_call_ms": ms, "algorithmic_flops_per_call": flops,
+                     "achieved_tflops": flops / (ms / 1e3) / 1e12,
+                     "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+        del x, wkv, wgate, ape, out
+    res["call"] = f"csa_compress_learned (hidden {D}, cmp_ratio {plan.r}, overlap), bf16 out"
+    res["steps"] = steps
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +287,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the sparse-MLA backward measurement")
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--no-kl", action="store_true", help="skip the indexer KL-loss gradient measurement")
+    ap.add_argument("--no-learned", action="store_true", help="skip the learned compressor measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -368,6 +409,8 @@ def main():
         result["backward"] = backward_bench(plan, pack, inputs, nwin, ncmp, args.bwd_steps, 2)
     if not args.no_kl and plan.topk_idx is not None and pack.H_I == 64 and pack.d_I == 128:
         result["indexer_kl"] = kl_bench(plan, pack, inputs, ncmp, args.bwd_steps, 2)
+    if not args.no_learned and plan.r == 4 and plan.Tc_cap > 0:
+        result["learned_compressor"] = learned_bench(plan, pack, args.bwd_steps, 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pack, args.cpu_budget)
     print(json.dumps(result), flush=True)
