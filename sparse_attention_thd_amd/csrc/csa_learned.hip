@@ -7,17 +7,19 @@
 //                       group has no previous group (kv 0, score -inf there)
 //   out[c, ch] = sum over positions of softmax(score[., ch]) kv[., ch]
 //
-// One GEMM tile per workgroup: 256 stream rows (64 groups) x 256 projection columns,
-// K = the hidden size in steps of 64 staged through LDS with global_load_lds_dwordx4.
-// Four wavefronts, each a 128 x 128 quarter as 4 x 4 v_mfma_f32_32x32x16_bf16
-// accumulators.  The tile's columns are weight rows chosen so that one accumulator
-// column holds, for one channel, every projection the pooling needs:
+// One GEMM tile per workgroup: 64 groups (256 stream rows) x 256 projection columns,
+// K = the hidden size in steps of 64 staged through LDS with global_load_lds_dwordx4,
+// two stages (one in flight).  Four wavefronts, each a 128 x 128 quarter as 4 x 4
+// v_mfma_f32_32x32x16_bf16 accumulators.  The tile's columns are weight rows chosen so
+// that one accumulator column holds, for one channel, every projection the pooling
+// needs:
 //   overlap:    column blocks [wkv ch, wkv hd + ch, wgate ch, wgate hd + ch] (32 ch)
 //   no overlap: column blocks [wkv ch, wgate ch, wkv ch + 32, wgate ch + 32]
-// An accumulator lane holds rows 8 q + 4 (lane / 32) + m, m < 4: whole groups, so
-// the pooling runs in registers; the previous group sits in the other lane half
-// (permlane32 swap) or, for a wavefront's first group, in the wavefront above it
-// (LDS).  With overlap a tile starts one group early and emits 63 groups.
+// and the first-half blocks (wkv ch, wgate ch) multiply the rows one group earlier
+// than the second-half blocks: the A stage holds the 4 rows before the tile too.  An
+// accumulator lane holds rows 8 q + 4 (lane / 32) + m, m < 4, i.e. whole groups, so
+// every lane finds its group's own second half and its previous group's first half in
+// its own registers, and the pooling runs there.
 #include "csa_common.h"
 #include "csa_internal.h"
 #include "csa_tile.h"
@@ -25,20 +27,43 @@
 namespace csa {
 namespace {
 
-constexpr int kLrRows = 256;                    // stream rows per tile (64 groups of 4)
-constexpr int kLrGroups = kLrRows / 4;
-constexpr int kLrK = 64;                        // hidden dims per K step (128-byte rows)
-constexpr int kLrStageA = kLrRows * kLrK * 2;   // 32 KiB
-constexpr int kLrStage = 2 * kLrStageA;         // A rows then B columns
-constexpr int kLrXchg = 2 * 2 * 4 * 32 * 4;     // [wn][kv, score][m][32 ch] float
+// Measured on the 16k pack at hidden size 4096: 64 dims per stage with two stages
+// beats 32 dims with three or four (fewer barriers per MFMA).
+constexpr int kLrGroups = 64;                       // groups per tile (256 stream rows)
+constexpr int kLrK = 64;                            // hidden dims per stage
+constexpr int kLrStages = 2;
+constexpr int kLrRB = kLrK * 2;                     // LDS row bytes
+constexpr int kLrRPI = 1024 / kLrRB;                // rows per load instruction (1 KiB)
+constexpr int kLrAinst = (260 + kLrRPI - 1) / kLrRPI;  // A: 4 leading rows + 256
+constexpr int kLrArows = kLrAinst * kLrRPI;
+constexpr int kLrBinst = 256 / kLrRPI;
+constexpr int kLrStageA = kLrArows * kLrRB;
+constexpr int kLrStageB = 256 * kLrRB;
+constexpr int kLrStage = kLrStageA + kLrStageB;
+constexpr int kLrAper = (kLrAinst - 1) / 4;         // A instructions per wavefront (+1 for wavefront 0)
+constexpr int kLrBper = kLrBinst / 4;
+constexpr int kLrPerStage = kLrAper + kLrBper;      // loads per stage (wavefront 0: one more)
+static_assert(kLrAinst == 4 * kLrAper + 1 && kLrBinst == 4 * kLrBper, "load split");
+static_assert(kLrStages * kLrStage <= 160 * 1024 - 1024, "LDS");
 
-// 16-byte chunk c of 128-byte LDS row R lives at chunk c ^ lsw(R): any 16 consecutive
-// rows read at one logical chunk touch 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int lsw(int R) { return (R >> 1) & 7; }
+// 16-byte chunk c of LDS row L lives at chunk c ^ lsw(L): any 16 consecutive rows
+// read at one logical chunk touch 16 distinct 16-byte bank groups (of 256 bytes).
+__device__ __forceinline__ int lsw(int L) { return (L / (256 / kLrRB)) & (kLrRB / 16 - 1); }
 
-__device__ __forceinline__ float other_half(float v, int h) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(h ? r[0] : r[1]);
+// s_waitcnt vmcnt(V) (expcnt and lgkmcnt not waited on)
+template <int V>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | 0x0F70);
+}
+
+// wait until at most `later` stages' loads (n per stage) are outstanding
+template <int N>
+__device__ __forceinline__ void wait_stages(int later) {
+  if (later >= 3) wait_vm<3 * N>();
+  else if (later == 2) wait_vm<2 * N>();
+  else if (later == 1) wait_vm<N>();
+  else wait_vm<0>();
 }
 
 template <bool OVERLAP>
@@ -46,9 +71,10 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
     const uint16_t* __restrict__ x, int D, const uint16_t* __restrict__ wkv, const uint16_t* __restrict__ wgate,
     const float* __restrict__ ape, int hd, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
     int B, int Tc_cap, int n_mt, int n_nt, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kLrStage + kLrXchg];
-  __shared__ int32_t s_base[kLrGroups];
-  __shared__ int32_t s_first[kLrGroups];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLrStages * kLrStage];
+  __shared__ int32_t s_base[kLrArows / 4];  // entry e: group G0 - 1 + e
+  __shared__ int32_t s_first[kLrArows / 4];
+  static_assert(kLrArows / 4 <= kThreads, "table fill");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -62,11 +88,11 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
   if (item >= total) return;
   const int mt = item / n_nt, nt = item % n_nt;
   const int Tc = min(cu_cmp[B], Tc_cap);
-  const int G0 = OVERLAP ? mt * (kLrGroups - 1) - 1 : mt * kLrGroups;
-  if (G0 + (OVERLAP ? 1 : 0) >= Tc) return;
+  const int G0 = mt * kLrGroups;
+  if (G0 >= Tc) return;
 
-  if (tid < kLrGroups) {
-    const int c = G0 + tid;
+  if (tid < kLrArows / 4) {
+    const int c = G0 - 1 + tid;
     int base = 0, first = 0;
     if (c >= 0 && c < Tc) {
       const int b = segment_of(cu_cmp, B, c);
@@ -74,49 +100,64 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
       base = cu_kv[b] + 4 * j;
       first = j == 0;
     }
-    s_base[tid] = base;  // groups outside [0, Tc) read rows 0..3 and are not written
+    s_base[tid] = base;  // groups outside [0, Tc) read rows 0..3; their results are unused
     s_first[tid] = first;
   }
   __syncthreads();
 
-  // ---- per-lane load offsets: wavefront w fills LDS rows 64 w + 8 v + lane / 8
-  // (v < 8) of the A rows and of the B columns, chunk lane % 8
+  // ---- per-lane load offsets.  One load instruction fills kLrRPI LDS rows: lane l ->
+  // row kLrRPI u + l / (64 / kLrRPI), 16-byte chunk l % (64 / kLrRPI).  A: instructions
+  // u = wave + 4 v and, for wavefront 0, the last one as well; B: u = wave + 4 v.
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(lds)));
   const int chs = OVERLAP ? nt * 64 + 32 * wn : nt * 128 + 64 * wn;  // this wavefront's first channel
-  uint32_t aoff[8], boff[8];
+  const bool extra = wave == 0;  // wavefront 0 also loads the last A instruction
+  constexpr int CPR = kLrRB / 16;  // chunks per row
+  uint32_t aoff[kLrAper + 1], boff[kLrBper];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
-    const int R = 64 * wave + 8 * v + (lane >> 3);
-    const int src = (lane & 7) ^ lsw(R);
-    aoff[v] = static_cast<uint32_t>(s_base[R >> 2] + (R & 3)) * static_cast<uint32_t>(2 * D) +
+  for (int v = 0; v <= kLrAper; ++v) {
+    const int u = (v < kLrAper) ? wave + 4 * v : kLrAinst - 1;
+    const int L = kLrRPI * u + lane / CPR;
+    const int src = (lane % CPR) ^ lsw(L);
+    aoff[v] = static_cast<uint32_t>(s_base[L >> 2] + (L & 3)) * static_cast<uint32_t>(2 * D) +
               static_cast<uint32_t>(src * 16);
-    // B column R: wavefront pair (R / 128), block (R / 32) % 4, channel offset R % 32
-    const int nb = (R >> 5) & 3, i = R & 31;
-    const int cwn = R >> 7;
+  }
+#pragma unroll
+  for (int v = 0; v < kLrBper; ++v) {
+    const int u = wave + 4 * v;
+    const int Rb = kLrRPI * u + lane / CPR;  // tile column
+    const int src = (lane % CPR) ^ lsw(Rb);
+    const int nb = (Rb >> 5) & 3, i = Rb & 31, cwn = Rb >> 7;
     int wrow;
     if (OVERLAP) wrow = nt * 64 + 32 * cwn + i + ((nb & 1) ? hd : 0);
     else wrow = nt * 128 + 64 * cwn + i + ((nb >> 1) ? 32 : 0);
     boff[v] = static_cast<uint32_t>(wrow * D * 2 + src * 16);
   }
-  // B column blocks of this wavefront's loads: (64 w + 8 v) / 32 % 4 = 2 (w % 2) + v / 4
   auto stage = [&](int ks, int bf) {
     const unsigned char* xa = reinterpret_cast<const unsigned char*>(x) + ks * kLrK * 2;
     const uint32_t la = lds0 + static_cast<uint32_t>(bf * kLrStage);
 #pragma unroll
-    for (int v = 0; v < 8; ++v) row_to_lds(xa, aoff[v], la + static_cast<uint32_t>((8 * wave + v) * 1024));
+    for (int v = 0; v < kLrAper; ++v)
+      row_to_lds(xa, aoff[v], la + static_cast<uint32_t>((wave + 4 * v) * 1024));
+    if (extra) row_to_lds(xa, aoff[kLrAper], la + static_cast<uint32_t>((kLrAinst - 1) * 1024));
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int nb = 2 * (wave & 1) + (v >> 2);
+    for (int v = 0; v < kLrBper; ++v) {
+      const int u = wave + 4 * v;
+      const int nb = ((kLrRPI * u) >> 5) & 3;  // column block of rows kLrRPI u ..
       const bool gate = OVERLAP ? (nb >= 2) : (nb & 1);
       const unsigned char* wb = reinterpret_cast<const unsigned char*>(gate ? wgate : wkv) + ks * kLrK * 2;
-      row_to_lds(wb, boff[v], la + static_cast<uint32_t>(kLrStageA + (8 * wave + v) * 1024));
+      row_to_lds(wb, boff[v], la + static_cast<uint32_t>(kLrStageA + u * 1024));
     }
   };
 
-  // fragment offsets: row (or column) 32 blk + lane % 32 of the quarter, k-chunk 2 s + h
-  uint32_t foff[4];
+  // fragment offsets: row 32 blk + lane % 32 (+ 4 for the group-aligned A rows), chunk 2 s + h
+  constexpr int NS = kLrK / 16;  // MFMA k-steps per stage
+  uint32_t fo_lo[NS], fo_hi[NS];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) foff[s] = static_cast<uint32_t>((lane & 31) * 128 + (((2 * s + h) ^ lsw(lane & 31)) * 16));
+  for (int s = 0; s < NS; ++s) {
+    const int r0 = lane & 31, r1 = r0 + 4;
+    fo_lo[s] = static_cast<uint32_t>(r0 * kLrRB + (((2 * s + h) ^ lsw(r0)) * 16));
+    fo_hi[s] = static_cast<uint32_t>(r1 * kLrRB + (((2 * s + h) ^ lsw(r1)) * 16));
+  }
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -127,32 +168,41 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
   const int nk = D / kLrK;
-  stage(0, 0);
-  for (int ks = 0; ks < nk; ++ks) {
-    const int bf = ks & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's rows of step ks landed
-    tile_barrier();                      // ... and everyone's; buffer bf ^ 1 is free
-    if (ks + 1 < nk) stage(ks + 1, bf ^ 1);
-    const unsigned char* A = lds + bf * kLrStage + wm * 128 * 128;
-    const unsigned char* Bm = lds + bf * kLrStage + kLrStageA + wn * 128 * 128;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 a[4], b[4];
+  for (int st = 0; st < kLrStages - 1; ++st)
+    if (st < nk) stage(st, st);
+  for (int ks = 0; ks < nk; ++ks) {
+    // this wavefront's rows of stage ks have landed once only the later stages' loads
+    // remain (kLrPerStage + 1 instructions per stage for wavefront 0)
+    const int later = min(nk - 1 - ks, kLrStages - 2);
+    if (extra) wait_stages<kLrPerStage + 1>(later);
+    else wait_stages<kLrPerStage>(later);
+    tile_barrier();  // everyone's rows landed; the buffer of stage ks - 1 is free
+    if (ks + kLrStages - 1 < nk) stage(ks + kLrStages - 1, (ks + kLrStages - 1) % kLrStages);
+    const unsigned char* A = lds + (ks % kLrStages) * kLrStage + wm * 128 * kLrRB;
+    const unsigned char* Bm = lds + (ks % kLrStages) * kLrStage + kLrStageA + wn * 128 * kLrRB;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 alo[4], ahi[4], b[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        a[q] = *reinterpret_cast<const bf16x8*>(A + q * 32 * 128 + foff[s]);
-        b[q] = *reinterpret_cast<const bf16x8*>(Bm + q * 32 * 128 + foff[s]);
+        ahi[q] = *reinterpret_cast<const bf16x8*>(A + q * 32 * kLrRB + fo_hi[s]);
+        if (OVERLAP) alo[q] = *reinterpret_cast<const bf16x8*>(A + q * 32 * kLrRB + fo_lo[s]);
+        b[q] = *reinterpret_cast<const bf16x8*>(Bm + q * 32 * kLrRB + fo_lo[s]);
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
+        for (int nb = 0; nb < 4; ++nb) {
+          const bf16x8 a = (OVERLAP && (nb == 0 || nb == 2)) ? alo[mb] : ahi[mb];
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[nb], acc[mb][nb], 0, 0, 0);
+        }
     }
   }
 
   // ---- pooling epilogue.  Lane (h, l % 32): channel(s) chs + l % 32 (+ 32), groups
-  // gi = 32 wm + 8 mb + 2 q + h, positions m = 0..3 in acc[mb][.][4 q + m].
+  // gi = 32 wm + 8 mb + 2 q + h, positions m = 0..3 in acc[mb][.][4 q + m]; with overlap
+  // blocks 0 and 2 hold the previous group's rows.
   const int cl = lane & 31;
   if (OVERLAP) {
     const int ch = chs + cl;
@@ -163,55 +213,19 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
       ape_lo[m] = ape[m * C + ch];
       ape_hi[m] = ape[m * C + hd + ch];
     }
-    // the wavefront's first group takes its previous group from the wavefront above
-    float* xch = reinterpret_cast<float*>(lds + 2 * kLrStage);  // not touched by the K loop
-    if (wm == 0 && h == 1) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        xch[((wn * 2 + 0) * 4 + m) * 32 + cl] = acc[3][0][12 + m];
-        xch[((wn * 2 + 1) * 4 + m) * 32 + cl] = acc[3][2][12 + m];
-      }
-    }
-    __syncthreads();
-    float up_kv[4], up_sc[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      up_kv[m] = xch[((wn * 2 + 0) * 4 + m) * 32 + cl];
-      up_sc[m] = xch[((wn * 2 + 1) * 4 + m) * 32 + cl];
-    }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int gi = 32 * wm + 8 * mb + 2 * q + h;
-        float pkv[4], psc[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // previous group: h = 1 -> (mb, q) of lane - 32; h = 0 -> (mb, q - 1) of lane + 32
-          const float o_same_kv = other_half(acc[mb][0][4 * q + m], h);
-          const float o_same_sc = other_half(acc[mb][2][4 * q + m], h);
-          float o_prev_kv, o_prev_sc;
-          if (q > 0) {
-            o_prev_kv = other_half(acc[mb][0][4 * q - 4 + m], h);
-            o_prev_sc = other_half(acc[mb][2][4 * q - 4 + m], h);
-          } else if (mb > 0) {
-            o_prev_kv = other_half(acc[mb - 1][0][12 + m], h);
-            o_prev_sc = other_half(acc[mb - 1][2][12 + m], h);
-          } else {
-            o_prev_kv = up_kv[m];
-            o_prev_sc = up_sc[m];
-          }
-          pkv[m] = h ? o_same_kv : o_prev_kv;
-          psc[m] = (h ? o_same_sc : o_prev_sc) + ape_lo[m];
-        }
         const int c = G0 + gi;
-        if (gi == 0 || c >= Tc) continue;  // the tile's leading group only feeds the next one
-        const bool first = s_first[gi] != 0;
+        if (c >= Tc) continue;
+        const bool first = s_first[gi + 1] != 0;
         float sc[8], kvv[8];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          sc[m] = first ? -__builtin_huge_valf() : psc[m];
-          kvv[m] = first ? 0.f : pkv[m];
+          sc[m] = first ? -__builtin_huge_valf() : acc[mb][2][4 * q + m] + ape_lo[m];
+          kvv[m] = first ? 0.f : acc[mb][0][4 * q + m];
           sc[4 + m] = acc[mb][3][4 * q + m] + ape_hi[m];
           kvv[4 + m] = acc[mb][1][4 * q + m];
         }
@@ -271,8 +285,7 @@ hipError_t launch_compress_learned(const void* x, int Tkv, int D, const void* wk
                                    const float* ape, int hd, int overlap, const int32_t* cu_kv,
                                    const int32_t* cu_cmp, int B, void* out, int Tc_cap, hipStream_t s) {
   if (Tc_cap <= 0 || Tkv <= 0) return hipSuccess;  // nothing to launch
-  const int per_tile = overlap ? kLrGroups - 1 : kLrGroups;
-  const int n_mt = (Tc_cap + per_tile - 1) / per_tile;
+  const int n_mt = (Tc_cap + kLrGroups - 1) / kLrGroups;
   const int n_nt = hd / (overlap ? 64 : 128);
   const long long total = static_cast<long long>(n_mt) * n_nt;
   const long long grid = (total + 7) / 8 * 8;

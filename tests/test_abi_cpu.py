@@ -86,7 +86,7 @@ def _learned(**kw):
     (dict(x=None), EINVAL), (dict(wkv=None), EINVAL), (dict(wgate=None), EINVAL), (dict(ape=None), EINVAL),
     (dict(out=None), EINVAL), (dict(cu_cmp=None), EINVAL), (dict(B=0), EINVAL), (dict(D=0), EINVAL),
     (dict(hd=0), EINVAL), (dict(r=0), EINVAL), (dict(overlap=2), EINVAL), (dict(dtype=7), EINVAL),
-    (dict(Tc_cap=3), EINVAL), (dict(r=8, Tc_cap=2), EUNSUP), (dict(D=4000), EUNSUP), (dict(hd=96), EUNSUP),
+    (dict(Tc_cap=3), EINVAL), (dict(r=8, Tc_cap=2), EUNSUP), (dict(D=4000), EUNSUP), (dict(D=32), EUNSUP), (dict(hd=96), EUNSUP),
     (dict(hd=64, overlap=0), EUNSUP), (dict(dtype=0), EUNSUP), (dict(Tkv=1 << 20, Tc_cap=1 << 18), EUNSUP),
 ])
 def test_compress_learned_rejects(kw, code):

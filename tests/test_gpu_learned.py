@@ -90,6 +90,8 @@ CASES = [
     ("many_segs", dict(D=1024, hd=128, overlap=True)),
     ("empty_segs", dict(D=192, hd=192, overlap=True)),
     ("tiles", dict(D=320, hd=128, overlap=True, gate_scale=24.0, ape_scale=6.0)),  # peaky softmax
+    ("small", dict(D=64, hd=64, overlap=True)),      # one K step
+    ("empty_segs", dict(D=128, hd=128, overlap=False)),  # two K steps
 ]
 
 
