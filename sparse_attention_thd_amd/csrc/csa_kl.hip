@@ -79,16 +79,26 @@ __device__ __forceinline__ float block_max(float v, float* red) {
 
 // ----------------------------------------------------------------------------- per query
 
-template <int NC>  // cmp_idx row chunks of kThreads entries
+// s_waitcnt vmcnt(2 * later): at most `later` later steps' gathers (two per
+// wavefront each) still in flight
+__device__ __forceinline__ void wait_gathers(int later) {
+  if (later >= 2) __builtin_amdgcn_s_waitcnt(0x0F74);
+  else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0F72);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+template <int NC, int KB>  // cmp_idx row chunks of kThreads entries; K stage buffers
 __global__ __launch_bounds__(kThreads) void kl_query_kernel(
     const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp,
     const int32_t* __restrict__ cmp_idx, const float* __restrict__ attn_l1, int topk, int Tq, int Tc,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B,
     int global_start, int r, float loss_scale, uint16_t* __restrict__ d_q, float* __restrict__ d_w,
     float* __restrict__ loss, void* ws_base, int nvis_cap) {
-  __shared__ __attribute__((aligned(1024))) unsigned char kst[2][kKlRows * 256];
-  __shared__ int32_t crow[kMaxTopk];
-  __shared__ float sI[kWaves][kMaxTopk];  // per-wavefront partial scores; row 0 then holds G
+  static_assert(KB >= 2 && KB <= 3, "stage buffers");
+  constexpr int kCap = NC * kThreads;  // largest selection this instance handles
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[KB][kKlRows * 256];
+  __shared__ int32_t crow[kCap];
+  __shared__ float sI[kWaves][kCap];  // per-wavefront partial scores; row 0 then holds G
   __shared__ uint32_t wsum[kWaves];
   __shared__ float red[kWaves];
 
@@ -113,6 +123,10 @@ __global__ __launch_bounds__(kThreads) void kl_query_kernel(
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qb[ks] = *reinterpret_cast<const bf16x8*>(qrow + 32 * ks);
   const float wh = bf16_bits_to_f32(w[static_cast<long long>(i) * 64 + head]);
+  // pass 1 takes u = q . K^T (heads 16 w + 4 g + j of row n in lane (n, g)): their weights
+  float wq[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wq[j] = bf16_bits_to_f32(w[static_cast<long long>(i) * 64 + 16 * wave + 4 * g + j]);
 
   // segment and visible compressed range
   int count = 0;
@@ -161,26 +175,32 @@ __global__ __launch_bounds__(kThreads) void kl_query_kernel(
     }
   };
 
-  // ---- pass 1: scores
-  if (nsteps > 0) stage(0, 0);
+  // ---- pass 1: scores.  KB - 1 steps of gathers in flight; the bare barrier keeps
+  // the later steps' gathers outstanding across it.
+#pragma unroll
+  for (int d = 0; d < KB - 1; ++d)
+    if (d < nsteps) stage(d, d);
   for (int sb = 0; sb < nsteps; ++sb) {
-    const int bf = sb & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();  // step sb landed; buffer bf ^ 1 is free
-    if (sb + 1 < nsteps) stage(sb + 1, bf ^ 1);
+    const int bf = sb % KB;
+    wait_gathers(min(nsteps - 1 - sb, KB - 2));
+    tile_barrier();  // step sb landed everywhere; the buffer of step sb - 1 is free
+    if (sb + KB - 1 < nsteps) stage(sb + KB - 1, (sb + KB - 1) % KB);
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
-      f32x4 acc;
-      scores(kst[bf], cb, acc);
+      // u[16 heads x 16 rows] = q . K^T: the same fragments as u^T with the operands
+      // swapped; the head sum is then four in-lane terms and one 4-lane reduction
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int rr = 16 * cb + n;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v = wh * fmaxf(acc[j], 0.f);
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 4, 64);
-        v += __shfl_xor(v, 8, 64);
-        if (n == 0) sI[wave][sb * kKlRows + 16 * cb + 4 * g + j] = v;
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kst[bf] + rr * 256 + kchunk(rr, 4 * ks + g) * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ks], kf, acc, 0, 0, 0);
       }
+      float v = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v += wq[j] * fmaxf(acc[j], 0.f);
+      v = quad_sum(v);
+      if (g == 0) sI[wave][sb * kKlRows + rr] = v;
     }
   }
   __syncthreads();
@@ -220,12 +240,14 @@ __global__ __launch_bounds__(kThreads) void kl_query_kernel(
   // K^T transpose reads: source lane m of lane group g points at stage row 4 g + m / 4
   // (+ 16 for the second row block), dims 16 db + 4 (m % 4)
   const int trow = 4 * g + (n >> 2);
-  if (live && nsteps > 0) stage(0, 0);
+#pragma unroll
+  for (int d = 0; d < KB - 1; ++d)
+    if (live && d < nsteps) stage(d, d);
   for (int sb = 0; live && sb < nsteps; ++sb) {
-    const int bf = sb & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __syncthreads();
-    if (sb + 1 < nsteps) stage(sb + 1, bf ^ 1);
+    const int bf = sb % KB;
+    wait_gathers(min(nsteps - 1 - sb, KB - 2));
+    tile_barrier();
+    if (sb + KB - 1 < nsteps) stage(sb + KB - 1, (sb + KB - 1) % KB);
     bf16x8 mfrag;
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
@@ -519,7 +541,10 @@ hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_
   const auto* q16 = static_cast<const uint16_t*>(q_I);
   const auto* w16 = static_cast<const uint16_t*>(w);
   const auto* k16 = static_cast<const uint16_t*>(k_cmp);
-  auto kq = (topk <= 2 * kThreads) ? kl_query_kernel<2> : kl_query_kernel<kMaxTopk / kThreads>;
+#ifndef CSA_KL_KB
+#define CSA_KL_KB 2
+#endif
+  auto kq = (topk <= 2 * kThreads) ? kl_query_kernel<2, CSA_KL_KB> : kl_query_kernel<kMaxTopk / kThreads, 2>;
   hipLaunchKernelGGL(kq, dim3(Tq), dim3(kThreads), 0, s, q16, w16, k16, cmp_idx, attn_l1, topk, Tq, Tc, cu_q, cu_kv,
                      cu_cmp, B, global_start, r, loss_scale, static_cast<uint16_t*>(d_q), d_w, loss, workspace,
                      nvis_cap);
