@@ -54,6 +54,8 @@ def _small(name):
         return pack_from_lengths("many_segs", [5 + (37 * k) % 120 for k in range(80)], seed=13, topk=32)
     if name == "stress_small":  # peaky softmax (q, kv ~ N(0,1))
         return pack_from_lengths("stress_small", [900], seed=14, topk=32, q_scale=1.0, kv_scale=1.0)
+    if name == "topk1024":  # the top-k > 512 instances (up to 650 kept rows per query)
+        return pack_from_lengths("topk1024", [2600, 150], seed=23, topk=1024)
     if name == "no_sinks":
         return dataclasses.replace(pack_from_lengths("no_sinks", [400, 90], seed=15, topk=32), sinks=None)
     raise KeyError(name)
@@ -124,7 +126,7 @@ def _oracle(pack, tabs, plan, dout, attend_all, slots, queries=None):
 
 
 SMALL = ["select16", "edges", "long", "short_only", "hca_small", "cp_small", "win_right", "no_compress",
-         "many_segs", "stress_small", "no_sinks"]
+         "many_segs", "stress_small", "no_sinks", "topk1024"]
 
 
 @pytest.mark.parametrize("name", SMALL)

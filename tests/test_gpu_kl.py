@@ -43,6 +43,8 @@ def _pack(name):
     if name == "cp_small":
         return pack_from_lengths("cp_small", [700, 1500, 900, 400], seed=8, q_rows=(1000, 2600), kv_rows=2600,
                                  topk=32)
+    if name == "topk1024":  # the top-k > 512 instance (up to 650 kept rows per query)
+        return pack_from_lengths("topk1024", [2600, 150], seed=23, topk=1024)
     raise KeyError(name)
 
 
@@ -127,7 +129,7 @@ def _check(pack, plan, p, scale, queries=None):
     return got
 
 
-@pytest.mark.parametrize("name", ["select16", "long", "edges", "many_segs", "cp_small"])
+@pytest.mark.parametrize("name", ["select16", "long", "edges", "many_segs", "cp_small", "topk1024"])
 def test_kl_grad_matches_oracle(name):
     pack = _pack(name)
     print(f"\n[case] {name}: Tq={pack.Tq} -> forward on GPU", flush=True)
