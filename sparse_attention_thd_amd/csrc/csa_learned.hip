@@ -10,7 +10,9 @@
 // One GEMM tile per workgroup: 64 groups (256 stream rows) x 256 projection columns,
 // K = the hidden size in steps of 64 staged through LDS with global_load_lds_dwordx4,
 // two stages (one in flight).  Four wavefronts, each a 128 x 128 quarter as 4 x 4
-// v_mfma_f32_32x32x16_bf16 accumulators.  The tile's columns are weight rows chosen so
+// v_mfma_f32_32x32x16_bf16 accumulators.  When that leaves CUs idle (fewer than 512
+// tiles) a half-height tile is used: 32 groups, 2 x 4 accumulators per wavefront, 32
+// dims per stage in three stages, two workgroups per CU.  The tile's columns are weight rows chosen so
 // that one accumulator column holds, for one channel, every projection the pooling
 // needs:
 //   overlap:    column blocks [wkv ch, wkv hd + ch, wgate ch, wgate hd + ch] (32 ch)
@@ -27,28 +29,37 @@
 namespace csa {
 namespace {
 
-// Measured on the 16k pack at hidden size 4096: 64 dims per stage with two stages
-// beats 32 dims with three or four (fewer barriers per MFMA).
-constexpr int kLrGroups = 64;                       // groups per tile (256 stream rows)
-constexpr int kLrK = 64;                            // hidden dims per stage
-constexpr int kLrStages = 2;
-constexpr int kLrRB = kLrK * 2;                     // LDS row bytes
-constexpr int kLrRPI = 1024 / kLrRB;                // rows per load instruction (1 KiB)
-constexpr int kLrAinst = (260 + kLrRPI - 1) / kLrRPI;  // A: 4 leading rows + 256
-constexpr int kLrArows = kLrAinst * kLrRPI;
-constexpr int kLrBinst = 256 / kLrRPI;
-constexpr int kLrStageA = kLrArows * kLrRB;
-constexpr int kLrStageB = 256 * kLrRB;
-constexpr int kLrStage = kLrStageA + kLrStageB;
-constexpr int kLrAper = (kLrAinst - 1) / 4;         // A instructions per wavefront (+1 for wavefront 0)
-constexpr int kLrBper = kLrBinst / 4;
-constexpr int kLrPerStage = kLrAper + kLrBper;      // loads per stage (wavefront 0: one more)
-static_assert(kLrAinst == 4 * kLrAper + 1 && kLrBinst == 4 * kLrBper, "load split");
-static_assert(kLrStages * kLrStage <= 160 * 1024 - 1024, "LDS");
-
-// 16-byte chunk c of LDS row L lives at chunk c ^ lsw(L): any 16 consecutive rows
-// read at one logical chunk touch 16 distinct 16-byte bank groups (of 256 bytes).
-__device__ __forceinline__ int lsw(int L) { return (L / (256 / kLrRB)) & (kLrRB / 16 - 1); }
+// Tile shape: MT stream rows (MT / 4 groups) x 256 projection columns, KS hidden dims
+// per LDS stage, NST stages.  Measured on the 16k pack at hidden size 4096: 64 dims per
+// stage with two stages beats 32 dims with three or four (fewer barriers per MFMA).
+template <int MT, int KS, int NST>
+struct LrCfg {
+  static constexpr int kMT = MT;
+  static constexpr int kMinBlocks = MT == 128 ? 2 : 1;          // workgroups per CU the registers must allow
+  static constexpr int kGroups = MT / 4;                        // groups per tile
+  static constexpr int kMB = MT / 64;                           // 32-row blocks per wavefront
+  static constexpr int kK = KS;
+  static constexpr int kStages = NST;
+  static constexpr int kRB = KS * 2;                            // LDS row bytes
+  static constexpr int kRPI = 1024 / kRB;                       // rows per load instruction (1 KiB)
+  static constexpr int kAinst = (MT + 4 + kRPI - 1) / kRPI;     // A: 4 leading rows + MT
+  static constexpr int kArows = kAinst * kRPI;
+  static constexpr int kBinst = 256 / kRPI;
+  static constexpr int kStageA = kArows * kRB;
+  static constexpr int kStageB = 256 * kRB;
+  static constexpr int kStage = kStageA + kStageB;
+  static constexpr int kAper = (kAinst - 1) / 4;                // A instructions per wavefront (+1 for wavefront 0)
+  static constexpr int kBper = kBinst / 4;
+  static constexpr int kPerStage = kAper + kBper;               // loads per stage (wavefront 0: one more)
+  static_assert(kAinst == 4 * kAper + 1 && kBinst == 4 * kBper, "load split");
+  static_assert(NST * kStage <= 160 * 1024 - 1024, "LDS");
+  static_assert(kArows / 4 <= kThreads, "table fill");
+  // 16-byte chunk c of LDS row L lives at chunk c ^ lsw(L): any 16 consecutive rows
+  // read at one logical chunk touch 16 distinct 16-byte bank groups (of 256 bytes).
+  __device__ static int lsw(int L) { return (L / (256 / kRB)) & (kRB / 16 - 1); }
+};
+using LrBig = LrCfg<256, 64, 2>;    // 64 groups per tile
+using LrSmall = LrCfg<128, 32, 3>;  // 32 groups per tile: twice the tiles, two workgroups per CU
 
 // s_waitcnt vmcnt(V) (expcnt and lgkmcnt not waited on)
 template <int V>
@@ -66,15 +77,19 @@ __device__ __forceinline__ void wait_stages(int later) {
   else wait_vm<0>();
 }
 
-template <bool OVERLAP>
-__global__ __launch_bounds__(kThreads) void learned_compress_kernel(
+template <bool OVERLAP, class Cfg>
+__global__ __launch_bounds__(kThreads, Cfg::kMinBlocks) void learned_compress_kernel(
     const uint16_t* __restrict__ x, int D, const uint16_t* __restrict__ wkv, const uint16_t* __restrict__ wgate,
     const float* __restrict__ ape, int hd, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
     int B, int Tc_cap, int n_mt, int n_nt, uint16_t* __restrict__ out) {
+  constexpr int kLrGroups = Cfg::kGroups, kLrK = Cfg::kK, kLrStages = Cfg::kStages, kLrRB = Cfg::kRB;
+  constexpr int kLrRPI = Cfg::kRPI, kLrAinst = Cfg::kAinst, kLrArows = Cfg::kArows, kLrStageA = Cfg::kStageA;
+  constexpr int kLrStage = Cfg::kStage, kLrAper = Cfg::kAper, kLrBper = Cfg::kBper, kLrPerStage = Cfg::kPerStage;
+  constexpr int MB = Cfg::kMB, HALF = Cfg::kMT / 2;  // 32-row blocks and rows per wavefront
+  auto lsw = [](int L) { return Cfg::lsw(L); };
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLrStages * kLrStage];
   __shared__ int32_t s_base[kLrArows / 4];  // entry e: group G0 - 1 + e
   __shared__ int32_t s_first[kLrArows / 4];
-  static_assert(kLrArows / 4 <= kThreads, "table fill");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -159,9 +174,9 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
     fo_hi[s] = static_cast<uint32_t>(r1 * kLrRB + (((2 * s + h) ^ lsw(r1)) * 16));
   }
 
-  f32x16 acc[4][4];
+  f32x16 acc[MB][4];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
@@ -179,19 +194,20 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
     else wait_stages<kLrPerStage>(later);
     tile_barrier();  // everyone's rows landed; the buffer of stage ks - 1 is free
     if (ks + kLrStages - 1 < nk) stage(ks + kLrStages - 1, (ks + kLrStages - 1) % kLrStages);
-    const unsigned char* A = lds + (ks % kLrStages) * kLrStage + wm * 128 * kLrRB;
+    const unsigned char* A = lds + (ks % kLrStages) * kLrStage + wm * HALF * kLrRB;
     const unsigned char* Bm = lds + (ks % kLrStages) * kLrStage + kLrStageA + wn * 128 * kLrRB;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      bf16x8 alo[4], ahi[4], b[4];
+      bf16x8 alo[MB], ahi[MB], b[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < MB; ++q) {
         ahi[q] = *reinterpret_cast<const bf16x8*>(A + q * 32 * kLrRB + fo_hi[s]);
         if (OVERLAP) alo[q] = *reinterpret_cast<const bf16x8*>(A + q * 32 * kLrRB + fo_lo[s]);
-        b[q] = *reinterpret_cast<const bf16x8*>(Bm + q * 32 * kLrRB + fo_lo[s]);
       }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int q = 0; q < 4; ++q) b[q] = *reinterpret_cast<const bf16x8*>(Bm + q * 32 * kLrRB + fo_lo[s]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
           const bf16x8 a = (OVERLAP && (nb == 0 || nb == 2)) ? alo[mb] : ahi[mb];
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
   }
 
   // ---- pooling epilogue.  Lane (h, l % 32): channel(s) chs + l % 32 (+ 32), groups
-  // gi = 32 wm + 8 mb + 2 q + h, positions m = 0..3 in acc[mb][.][4 q + m]; with overlap
+  // gi = (MT / 8) wm + 8 mb + 2 q + h, positions m = 0..3 in acc[mb][.][4 q + m]; with overlap
   // blocks 0 and 2 hold the previous group's rows.
   const int cl = lane & 31;
   if (OVERLAP) {
@@ -214,10 +230,10 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
       ape_hi[m] = ape[m * C + hd + ch];
     }
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int gi = 32 * wm + 8 * mb + 2 * q + h;
+        const int gi = (HALF / 4) * wm + 8 * mb + 2 * q + h;
         const int c = G0 + gi;
         if (c >= Tc) continue;
         const bool first = s_first[gi + 1] != 0;
@@ -250,10 +266,10 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
 #pragma unroll
       for (int m = 0; m < 4; ++m) ap[m] = ape[m * hd + ch];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = G0 + 32 * wm + 8 * mb + 2 * q + h;
+          const int c = G0 + (HALF / 4) * wm + 8 * mb + 2 * q + h;
           if (c >= Tc) continue;
           float sc[4], mx = -__builtin_huge_valf();
 #pragma unroll
@@ -278,29 +294,41 @@ __global__ __launch_bounds__(kThreads) void learned_compress_kernel(
 }  // namespace
 
 bool learned_shape_supported(int D, int hd, int cmp_ratio, int overlap, int dtype) {
-  return dtype == 1 && cmp_ratio == 4 && D >= kLrK && D % kLrK == 0 && hd > 0 && hd % (overlap ? 64 : 128) == 0;
+  return dtype == 1 && cmp_ratio == 4 && D >= 64 && D % 64 == 0 && hd > 0 && hd % (overlap ? 64 : 128) == 0;
+}
+
+template <class Cfg>
+static hipError_t launch_learned_cfg(const uint16_t* x, int D, const uint16_t* wk, const uint16_t* wg, const float* ape, int hd,
+                              int overlap, const int32_t* cu_kv, const int32_t* cu_cmp, int B, uint16_t* out,
+                              int Tc_cap, hipStream_t s) {
+  const int n_mt = (Tc_cap + Cfg::kGroups - 1) / Cfg::kGroups;
+  const int n_nt = hd / (overlap ? 64 : 128);
+  const long long total = static_cast<long long>(n_mt) * n_nt;
+  const long long grid = (total + 7) / 8 * 8;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (overlap)
+    hipLaunchKernelGGL((learned_compress_kernel<true, Cfg>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s,
+                       x, D, wk, wg, ape, hd, cu_kv, cu_cmp, B, Tc_cap, n_mt, n_nt, out);
+  else
+    hipLaunchKernelGGL((learned_compress_kernel<false, Cfg>), dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s,
+                       x, D, wk, wg, ape, hd, cu_kv, cu_cmp, B, Tc_cap, n_mt, n_nt, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_compress_learned(const void* x, int Tkv, int D, const void* wkv, const void* wgate,
                                    const float* ape, int hd, int overlap, const int32_t* cu_kv,
                                    const int32_t* cu_cmp, int B, void* out, int Tc_cap, hipStream_t s) {
   if (Tc_cap <= 0 || Tkv <= 0) return hipSuccess;  // nothing to launch
-  const int n_mt = (Tc_cap + kLrGroups - 1) / kLrGroups;
-  const int n_nt = hd / (overlap ? 64 : 128);
-  const long long total = static_cast<long long>(n_mt) * n_nt;
-  const long long grid = (total + 7) / 8 * 8;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const auto* x16 = static_cast<const uint16_t*>(x);
   const auto* wk = static_cast<const uint16_t*>(wkv);
   const auto* wg = static_cast<const uint16_t*>(wgate);
   auto* o16 = static_cast<uint16_t*>(out);
-  if (overlap)
-    hipLaunchKernelGGL(learned_compress_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, x16,
-                       D, wk, wg, ape, hd, cu_kv, cu_cmp, B, Tc_cap, n_mt, n_nt, o16);
-  else
-    hipLaunchKernelGGL(learned_compress_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s, x16,
-                       D, wk, wg, ape, hd, cu_kv, cu_cmp, B, Tc_cap, n_mt, n_nt, o16);
-  return hipGetLastError();
+  // the large tile unless it leaves CUs idle: 256 CUs take one large tile each
+  const long long big_tiles =
+      static_cast<long long>((Tc_cap + LrBig::kGroups - 1) / LrBig::kGroups) * (hd / (overlap ? 64 : 128));
+  if (big_tiles >= 2 * 256)
+    return launch_learned_cfg<LrBig>(x16, D, wk, wg, ape, hd, overlap, cu_kv, cu_cmp, B, o16, Tc_cap, s);
+  return launch_learned_cfg<LrSmall>(x16, D, wk, wg, ape, hd, overlap, cu_kv, cu_cmp, B, o16, Tc_cap, s);
 }
 
 }  // namespace csa
