@@ -185,6 +185,120 @@ __device__ void score_mfma_64x128(const uint16_t* __restrict__ q_I, const uint16
   }
 }
 
+// MFMA scoring of two queries of one segment (same candidate rows) in one pass: every
+// 16-candidate block of keys is loaded once and multiplied by both queries' q (128
+// register rows), which halves the key bytes per MFMA of the vector-memory path.
+__device__ void score_mfma_64x128_pair(const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w,
+                                       const uint16_t* __restrict__ k_cmp, int i0, int lo, int nv0, int nv1,
+                                       uint32_t* keys0, uint32_t* keys1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  bf16x8 qa[2][4][4];
+  float wv[2][4][4];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const uint16_t* qrow = q_I + static_cast<long long>(i0 + e) * 64 * 128;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qa[e][mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (16 * mb + n) * 128 + 32 * ks + 8 * g);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wv[e][mb][j] = bf16_bits_to_f32(w[static_cast<long long>(i0 + e) * 64 + 16 * mb + 4 * g + j]);
+  }
+  const int nvm = max(nv0, nv1);
+  const int nblk = (nvm + 15) >> 4;
+  for (int jb = wave; jb < nblk; jb += kWaves) {
+    const int c = 16 * jb + n;
+    bf16x8 kb[4];
+    if (c < nvm) {
+      const uint16_t* krow = k_cmp + static_cast<long long>(lo + c) * 128;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks + 8 * g);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kb[ks] = bf16x8{};
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float sc = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[e][mb][ks], kb[ks], acc, 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sc += wv[e][mb][j] * fmaxf(acc[j], 0.f);
+      }
+      sc += __shfl_xor(sc, 16, 64);
+      sc += __shfl_xor(sc, 32, 64);
+      if (g == 0 && c < (e ? nv1 : nv0)) (e ? keys1 : keys0)[c] = float_order_key(sc);
+    }
+  }
+}
+
+// (H_I, d_I) = (64, 128) bf16, two queries per workgroup: queries 2 x and 2 x + 1.
+// A query with no more candidates than top-k only writes its ascending list.  Two
+// selecting queries of one segment are scored in one pass (above); otherwise each is
+// scored alone.  The selections then run one after the other.
+__global__ __launch_bounds__(kThreads) void indexer_topk_pair_kernel(
+    const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B,
+    int global_start, int r, int cap, int topk, int Tq, int32_t* __restrict__ idx, float* __restrict__ score) {
+  extern __shared__ uint32_t dyn[];  // two key arrays of cap entries
+  __shared__ SelectShared sh;
+  const int i0 = 2 * static_cast<int>(blockIdx.x);
+  const int tid = threadIdx.x;
+  const int nq = min(2, Tq - i0);
+  int lo[2] = {0, 0}, nv[2] = {0, 0};
+  bool heavy[2] = {false, false};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (e >= nq) break;
+    const int i = i0 + e;
+    const int b = segment_of(cu_q, B, i);
+    const int p = global_start + i - cu_kv[b];
+    lo[e] = cu_cmp[b];
+    int v = (p + 1) / r;
+    v = min(v, cu_cmp[b + 1] - lo[e]);
+    nv[e] = max(0, min(v, cap));
+    heavy[e] = !(nv[e] <= topk && score == nullptr);
+    if (!heavy[e]) {
+      int32_t* out_idx = idx + static_cast<long long>(i) * topk;
+      for (int k = tid; k < topk; k += kThreads) out_idx[k] = (k < nv[e]) ? lo[e] + k : -1;
+    }
+  }
+  if (!heavy[0] && !heavy[1]) return;
+  uint32_t* keys[2] = {dyn, dyn + cap};
+  if (heavy[0] && heavy[1] && lo[0] == lo[1]) {
+    score_mfma_64x128_pair(q_I, w, k_cmp, i0, lo[0], nv[0], nv[1], keys[0], keys[1]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      if (heavy[e]) score_mfma_64x128(q_I, w, k_cmp, i0 + e, lo[e], nv[e], keys[e]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if (!heavy[e]) continue;
+    const int i = i0 + e;
+    int32_t* out_idx = idx + static_cast<long long>(i) * topk;
+    float* out_sc = score ? score + static_cast<long long>(i) * topk : nullptr;
+    if (nv[e] <= topk) {
+      for (int k = tid; k < topk; k += kThreads) {
+        out_idx[k] = (k < nv[e]) ? lo[e] + k : -1;
+        out_sc[k] = (k < nv[e]) ? order_key_to_float(keys[e][k]) : -__builtin_huge_valf();
+      }
+    } else {
+      select_and_emit(keys[e], nv[e], topk, lo[e], out_idx, out_sc, sh);
+    }
+    __syncthreads();  // the selection state is reused by the second query
+  }
+}
+
 template <int PATH, typename T>
 __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(const T* __restrict__ q_I, const T* __restrict__ w,
                                                                 const T* __restrict__ k_cmp, int H_I, int d_I,
@@ -243,13 +357,27 @@ hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp
   size_t lds = static_cast<size_t>(cap) * 4;
   if (!mfma) lds += static_cast<size_t>(H_I) * d_I * 4 + static_cast<size_t>(H_I) * 4;
   const dim3 grid(Tq), block(kThreads);
-  if (mfma) {
+  // Two queries per workgroup for long candidate lists, where halving the key bytes per
+  // MFMA pays for the lower occupancy and the back-to-back selections (measured: the
+  // 22999-token CP share 2.63 -> 2.31 ms; with lists of about 1000 candidates, as in the
+  // 16k pack, one query per workgroup is faster), and only while the two key arrays
+  // leave room for two workgroups per CU.
+  const bool pair = cap >= 2048 && 2 * static_cast<size_t>(cap) * 4 <= 64 * 1024;
+  if (mfma && !pair) {
     auto k = indexer_topk_kernel<1, uint16_t>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                         static_cast<int>(lds));
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
                        static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r,
                        cap, topk, idx, score);
+  } else if (mfma) {
+    auto k = indexer_topk_pair_kernel;
+    const size_t lds2 = 2 * static_cast<size_t>(cap) * 4;
+    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                        static_cast<int>(lds2));
+    hipLaunchKernelGGL(k, dim3((Tq + 1) / 2), block, lds2, s, static_cast<const uint16_t*>(q_I),
+                       static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(k_cmp), cu_q, cu_kv, cu_cmp, B,
+                       global_start, r, cap, topk, Tq, idx, score);
   } else if (dtype == 1) {
     auto k = indexer_topk_kernel<0, uint16_t>;
     hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
