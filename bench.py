@@ -142,6 +142,21 @@ def cpu_baseline(pack, budget_s=15.0):
                       f"extrapolated per query to the whole pack"}
 
 
+def gather_phases(plan, pack, ms):
+    """Indices + the two compressions as HBM traffic: algorithmic bytes are the index
+    tables written (q_seg, q_pos, q_cmp_lo, q_cmp_nvis: 16 B and the window slots 4 W B per
+    query, 4 B per compressed row) and, per compressed row, r rows read and one written
+    for the latent (d) and for the indexer keys (d_I)."""
+    Tc = int(plan.cu_seqlens_cmp[-1].item())
+    W = plan.wl + plan.wr + 1
+    idx_bytes = pack.Tq * (16 + 4 * W) + 4 * Tc
+    cmp_bytes = Tc * (plan.r + 1) * 2 * (pack.d + (pack.d_I if plan.k_I_cmp is not None else 0))
+    total = idx_bytes + cmp_bytes
+    gbs = total / (ms / 1e3) / 1e9
+    return {"calls": "csa_build_indices + csa_compress (latent, indexer keys)", "avg_ms": ms,
+            "algorithmic_bytes": total, "achieved_GBps": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
+
+
 def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
     """csa_sparse_mla_bwd on the forward's output and lse with a seeded bf16 dout.
 
@@ -401,6 +416,7 @@ def main():
                      "avg_launch_ms": mla_ms},
         "phases_ms": {"indices+compress": float(t_front.mean()), "indexer_topk": idx_ms, "sparse_mla": mla_ms,
                       "step_p10": float(np.percentile(t_step, 10)), "step_p90": float(np.percentile(t_step, 90))},
+        "gather_phases": gather_phases(plan, pack, float(t_front.mean())),
         "indexer": {"needed_score_flops": idx_flops,
                     "mfma_frac": (idx_flops / (idx_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS) if idx_ms > 0 else None},
         "host_wall_s": wall,
