@@ -10,6 +10,11 @@ The compressed branch follows the layer's compression mode (page "MindSpeed-LLM
 pull 4842", 主要改动, LayerCompressMode): ratio 4 runs the lightning indexer,
 another ratio above 1 attends every causally complete compressed row, ratio 1
 (or a pack whose segments are all shorter than the ratio) keeps only the window.
+
+Compressed rows are the segment-local mean of r rows by default; ``run`` can take
+``LearnedCompressor`` parameters instead (the gated overlapping compressor of page
+"PR #2038 完整报告", 关键源码片段 compressor.py), computed from the hidden rows ``x``
+with csa_compress_learned, for the latent rows, the indexer keys, or both.
 """
 from __future__ import annotations
 
@@ -33,6 +38,25 @@ def layer_compress_mode(cmp_ratio: int) -> LayerCompressMode:
     if cmp_ratio == 4:
         return LayerCompressMode.INDEXER
     return LayerCompressMode.COMPRESSOR_ONLY
+
+
+@dataclasses.dataclass
+class LearnedCompressor:
+    """Parameters of one learned compressor: wkv, wgate [C, D] (call dtype), ape [r, C] float32,
+    C = 2 * hd with overlap, hd otherwise."""
+    wkv: torch.Tensor
+    wgate: torch.Tensor
+    ape: torch.Tensor
+    overlap: bool = True
+
+    def hd(self) -> int:
+        C = int(self.wkv.shape[0])
+        return C // 2 if self.overlap else C
+
+    def run(self, x, layout, cu_seqlens_cmp, cmp_ratio, out, Tc_cap, stream=None):
+        _lib.csa_compress_learned(x, layout.Tkv, int(x.shape[1]), self.wkv, self.wgate, self.ape, self.hd(),
+                                  self.overlap, layout.cu_seqlens_kv, cu_seqlens_cmp, layout.B, cmp_ratio, out, Tc_cap,
+                                  stream)
 
 
 @dataclasses.dataclass
@@ -95,18 +119,33 @@ class CsaPlan:
         self.out = torch.empty((Tq, H, d), dtype=dtype, device=dev)
         self.lse = torch.empty((Tq, H), dtype=torch.float32, device=dev) if return_lse else None
 
-    def run(self, q, ori_kv, sinks=None, q_I=None, k_I=None, w=None, stream=None):
+    def run(self, q, ori_kv, sinks=None, q_I=None, k_I=None, w=None, stream=None, x=None,
+            kv_compressor: LearnedCompressor | None = None, key_compressor: LearnedCompressor | None = None):
+        """Enqueue the forward.  With ``kv_compressor`` / ``key_compressor`` the compressed
+        latent rows / indexer keys come from the hidden rows ``x`` [Tkv, D] through the
+        learned compressor instead of the mean of ori_kv / k_I."""
         L = self.L
+        if (kv_compressor is not None or key_compressor is not None) and x is None:
+            raise ValueError("a learned compressor needs the hidden rows x")
+        for comp, width, name in ((kv_compressor, self.d, "kv_compressor"), (key_compressor, self.d_I, "key_compressor")):
+            if comp is not None and comp.hd() != width:
+                raise ValueError(f"{name} produces {comp.hd()} channels, the plan needs {width}")
         _lib.csa_build_indices(L.cu_seqlens_q, L.cu_seqlens_kv, L.B, L.Tq, L.Tkv, L.global_start, self.r, self.wl,
                                self.wr, self.q_seg, self.q_pos, self.win_idx, self.cu_seqlens_cmp, self.cmp_residual,
                                self.q_cmp_lo, self.q_cmp_nvis, self.cmp_group, self.Tc_cap, stream)
         if self.cmp_kv is not None:
-            _lib.csa_compress(ori_kv, L.Tkv, self.d, L.cu_seqlens_kv, self.cu_seqlens_cmp, L.B, self.r, self.cmp_kv,
-                              self.Tc_cap, stream)
+            if kv_compressor is not None:
+                kv_compressor.run(x, L, self.cu_seqlens_cmp, self.r, self.cmp_kv, self.Tc_cap, stream)
+            else:
+                _lib.csa_compress(ori_kv, L.Tkv, self.d, L.cu_seqlens_kv, self.cu_seqlens_cmp, L.B, self.r,
+                                  self.cmp_kv, self.Tc_cap, stream)
         cmp_idx = None
         if self.mode == LayerCompressMode.INDEXER:
-            _lib.csa_compress(k_I, L.Tkv, self.d_I, L.cu_seqlens_kv, self.cu_seqlens_cmp, L.B, self.r, self.k_I_cmp,
-                              self.Tc_cap, stream)
+            if key_compressor is not None:
+                key_compressor.run(x, L, self.cu_seqlens_cmp, self.r, self.k_I_cmp, self.Tc_cap, stream)
+            else:
+                _lib.csa_compress(k_I, L.Tkv, self.d_I, L.cu_seqlens_kv, self.cu_seqlens_cmp, L.B, self.r,
+                                  self.k_I_cmp, self.Tc_cap, stream)
             _lib.csa_indexer_topk(q_I, w, self.k_I_cmp, L.Tq, self.H_I, self.d_I, L.cu_seqlens_q, L.cu_seqlens_kv,
                                   self.cu_seqlens_cmp, L.B, L.global_start, self.r, L.max_seqlen_kv, self.topk,
                                   self.topk_idx, self.topk_score, stream)

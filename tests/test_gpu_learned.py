@@ -133,3 +133,43 @@ def test_learned_compressor_pack16k_sampled_segments():
             s, e = int(cu_kv[b]), int(cu_kv[b + 1])
             ref = _ref(np.array([0, e - s]), ci, x_rows=ci.x[s:e])
             _close(bits[int(cmp_cu[b]):int(cmp_cu[b + 1])], ref, f"hd{hd} segment {b} ({e - s} rows)")
+
+
+def test_plan_with_learned_compressors():
+    """CsaPlan.run with learned compressors for the latent rows and the indexer keys (hidden
+    size 256): compressed rows against the oracle, top-k sets against oracle scores of the
+    GPU's compressed keys, attention against the oracle on those rows and sets."""
+    import sparse_attention_thd_amd as s
+    from gpu_support import assert_out_close, check_topk_row, host_view, oracle_attention, oracle_tables
+    from synth import pack_from_lengths
+    pack = pack_from_lengths("learned_plan", [600, 300, 1201], seed=4, topk=16)
+    ckv = compressor_inputs(pack.Tkv, D=256, hd=512, overlap=True, seed=31)
+    ckey = compressor_inputs(pack.Tkv, D=256, hd=128, overlap=True, seed=32)
+    x = ckv.x  # both compressors read the same hidden rows
+    layout = s.ThdLayout.from_host(pack.cu_seqlens_q, pack.cu_seqlens_kv, pack.global_start)
+    plan = s.CsaPlan(layout, H=pack.H, d=pack.d, H_I=pack.H_I, d_I=pack.d_I, cmp_ratio=4, topk=pack.topk,
+                     softmax_scale=pack.softmax_scale, return_topk_score=True)
+    kvc = s.LearnedCompressor(to_device(ckv.wkv), to_device(ckv.wgate), to_device(ckv.ape))
+    keyc = s.LearnedCompressor(to_device(ckey.wkv), to_device(ckey.wgate), to_device(ckey.ape))
+    print("[case] learned_plan: CsaPlan.run with learned compressors", flush=True)
+    plan.run(to_device(pack.q), to_device(pack.ori_kv), sinks=to_device(pack.sinks), q_I=to_device(pack.q_I),
+             w=to_device(pack.w), x=to_device(x), kv_compressor=kvc, key_compressor=keyc)
+    torch.cuda.synchronize()
+    tabs = oracle_tables(pack)
+    Tc = int(tabs["cu_seqlens_cmp"][-1])
+    xf = bf16_bits_to_f32(x)
+    for got, ci, what in ((plan.cmp_kv, ckv, "latent"), (plan.k_I_cmp, ckey, "keys")):
+        ref = oracle.compress_learned(xf, bf16_bits_to_f32(ci.wkv), bf16_bits_to_f32(ci.wgate), ci.ape,
+                                      pack.cu_seqlens_kv, 4, True)
+        bits = got.view(torch.int16).cpu().numpy().view(np.uint16)[:Tc]
+        _close(bits, ref, what)
+    kc = cpu(plan.k_I_cmp)[:Tc].astype(np.float64)
+    idx = cpu(plan.topk_idx)
+    qI, w = host_view(pack, "q_I"), host_view(pack, "w")
+    for i in range(pack.Tq):
+        lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
+        sc = oracle.indexer_scores(qI[i], w[i], kc[lo:lo + nv]) if nv else np.zeros(0)
+        check_topk_row(idx[i], lo, nv, sc, pack.topk)
+    qs = list(range(0, pack.Tq, 5))
+    out, _ = oracle_attention(pack, tabs, qs, cpu(plan.cmp_kv)[:Tc].astype(np.float64), idx[qs], oracle.INDEXER)
+    print("   ", assert_out_close(cpu(plan.out)[qs], out), flush=True)
