@@ -176,3 +176,26 @@ def test_backward_pack16k_sampled_queries():
     assert np.abs(got["ori_l1"][qs] - ref["ori_l1"]).max() <= L1_ABS
     assert np.abs(got["cmp_l1"][qs] - ref["cmp_l1"]).max() <= L1_ABS
     assert np.all(np.isfinite(got["d_ori_kv"])) and np.all(np.isfinite(got["d_cmp_kv"]))
+
+
+def test_backward_empty_query_slice():
+    """Tq = 0: the row gradients and the sink gradient are overwritten with zeros."""
+    import sparse_attention_thd_amd as s
+    print("[case] Tq = 0 -> csa_sparse_mla_bwd", flush=True)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    cu_q, cu_kv, cu_cmp = (torch.tensor(v, **i32) for v in ([0, 0], [0, 64], [0, 16]))
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    kv, ckv = torch.randn((64, 512), **bf), torch.randn((16, 512), **bf)
+    nan = lambda *shape: torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    d_ori, d_cmp, d_s = nan(64, 512), nan(16, 512), nan(64)
+    sinks = torch.randn(64, dtype=torch.float32, device="cuda")
+    nb = s.csa_sparse_mla_bwd_workspace_bytes(0, 127, 0, ckv, torch.empty((0, 512), **i32), 512, 64, 4)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+    empty = torch.empty((0, 64, 512), **bf)
+    s.csa_sparse_mla_bwd(empty, kv, ckv, torch.empty((0, 512), **i32), 512, 0, 64, 16, 64, 512, cu_q, cu_kv, cu_cmp,
+                         1, 64, 4, 127, 0, 64, sinks, 512 ** -0.5, empty,
+                         torch.empty((0, 64), dtype=torch.float32, device="cuda"), empty, empty, d_ori, d_cmp, d_s,
+                         None, None, 0, ws)
+    torch.cuda.synchronize()
+    for t in (d_ori, d_cmp, d_s):
+        assert not t.isnan().any() and not t.any()

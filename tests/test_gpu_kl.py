@@ -182,3 +182,22 @@ def test_kl_grad_pack16k_sampled_queries():
     plan = run_pack(pack)
     tabs = oracle_tables(pack)
     _check(pack, plan, _targets(plan, 201), 1.0 / pack.Tq, queries=sample_queries(pack, tabs, n=64))
+
+
+def test_kl_grad_empty_query_slice():
+    """Tq = 0 (a CP share past every query): d_k is still overwritten with zeros."""
+    import sparse_attention_thd_amd as s
+    print("[case] Tq = 0 -> csa_indexer_kl_grad", flush=True)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    cu_q, cu_kv, cu_cmp = (torch.tensor(v, **i32) for v in ([0, 0], [0, 64], [0, 16]))
+    bf = dict(dtype=torch.bfloat16, device="cuda")
+    k = torch.randn((16, 128), **bf)
+    d_k = torch.full((16, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(1, dtype=torch.uint8, device="cuda")
+    s.csa_indexer_kl_grad(torch.empty((0, 64, 128), **bf), torch.empty((0, 64), **bf), k,
+                          torch.empty((0, 512), **i32), torch.empty((0, 512), dtype=torch.float32, device="cuda"),
+                          512, 0, 16, 64, 128, cu_q, cu_kv, cu_cmp, 1, 64, 4, 64, 1.0,
+                          torch.empty((0, 64, 128), **bf), torch.empty((0, 64), dtype=torch.float32, device="cuda"),
+                          d_k, None, ws)
+    torch.cuda.synchronize()
+    assert not d_k.isnan().any() and not d_k.any()

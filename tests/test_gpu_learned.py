@@ -173,3 +173,11 @@ def test_plan_with_learned_compressors():
     qs = list(range(0, pack.Tq, 5))
     out, _ = oracle_attention(pack, tabs, qs, cpu(plan.cmp_kv)[:Tc].astype(np.float64), idx[qs], oracle.INDEXER)
     print("   ", assert_out_close(cpu(plan.out)[qs], out), flush=True)
+
+
+def test_learned_compressor_without_complete_groups():
+    """Every segment shorter than the ratio: no compressed row, nothing written."""
+    cu_kv = np.array([0, 1, 3, 6, 7])
+    ci = compressor_inputs(7, D=64, hd=64, overlap=True, seed=14)
+    bits, Tc = _run(cu_kv, ci)
+    assert Tc == 0 and (bits == SENTINEL).all()
