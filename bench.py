@@ -307,8 +307,9 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU path is a design, "
-              f"not part of this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library runs one GPU's share "
+              f"(a context-parallel slice is an input layout); sharding across GPUs is not implemented",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

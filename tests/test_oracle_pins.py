@@ -53,7 +53,7 @@ def test_golden_layout(path):
         np.testing.assert_array_equal(np.asarray(out[k]), np.asarray(v), err_msg=k)
 
 
-def test_survey_config_check_values():
+def test_workload_check_values():
     # compressed layout of the 16k pack (lengths are never multiples of 4)
     p = make_pack("pack16k")
     cu_cmp, res, _ = oracle.segment_table(p.cu_seqlens_kv, 4)
