@@ -198,3 +198,19 @@ def test_indexer_kl_grad_workspace_size_formula():
 def test_validate_layout_rejects_bad_arguments():
     assert LIB.csa_validate_layout(None, FAKE, 1, 0, 0, 0, -1, None) == EINVAL
     assert LIB.csa_validate_layout(FAKE, FAKE, 0, 0, 0, 0, -1, None) == EINVAL
+
+
+def test_plan_rejects_learned_compressor_misuse_before_any_call():
+    """CsaPlan.run checks learned-compressor arguments on the host (CPU tensors here:
+    the checks fire before the first library call)."""
+    import torch
+    from sparse_attention_thd_amd import CsaPlan, LearnedCompressor, ThdLayout
+    layout = ThdLayout.from_host([0, 8], [0, 8], device="cpu")
+    plan = CsaPlan(layout, H=4, d=64, H_I=2, d_I=32, cmp_ratio=4, topk=4, dtype=torch.float32)
+    comp = LearnedCompressor(torch.zeros(128, 16), torch.zeros(128, 16), torch.zeros(4, 128))  # hd 64
+    assert comp.hd() == 64
+    assert LearnedCompressor(comp.wkv[:64], comp.wgate[:64], comp.ape[:, :64], overlap=False).hd() == 64
+    with pytest.raises(ValueError, match="hidden rows"):
+        plan.run(None, None, kv_compressor=comp)
+    with pytest.raises(ValueError, match="32"):
+        plan.run(None, None, x=torch.zeros(8, 16), key_compressor=comp)
