@@ -44,7 +44,20 @@ __global__ __launch_bounds__(kThreads) void segment_scan_kernel(const int32_t* _
   }
 }
 
-// blockIdx.y == 0: per-query tables; 1: window slots (one thread per slot); 2: compressed group ids.
+constexpr int kWinQueries = 16;  // queries per workgroup of the window-slot job (4 per wavefront)
+
+// Segment of row x (largest b < B with cu[b] <= x, cu[0] <= x) for a whole wavefront:
+// one coalesced load per 64 entries and a ballot count, result wave-uniform.
+__device__ __forceinline__ int segment_of_wave(const int32_t* __restrict__ cu, int B, int x) {
+  const int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < B; base += 64) count += __popcll(__ballot(base + lane < B && cu[base + lane] <= x));
+  return __builtin_amdgcn_readfirstlane(count - 1);
+}
+
+// One 1-D grid, three jobs by block range: [0, n0) per-query tables (one thread per
+// query); [n0, n0 + n1) window slots (one wavefront per query: the slots of a query are
+// one contiguous row, written 64 at a time); [n0 + n1, ...) compressed group ids.
 __global__ __launch_bounds__(kThreads) void layout_kernel(const int32_t* __restrict__ cu_q,
                                                           const int32_t* __restrict__ cu_kv,
                                                           const int32_t* __restrict__ cu_cmp, int B, int Tq,
@@ -53,12 +66,13 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(const int32_t* __restr
                                                           int32_t* __restrict__ win_idx,
                                                           int32_t* __restrict__ q_cmp_lo,
                                                           int32_t* __restrict__ q_cmp_nvis,
-                                                          int32_t* __restrict__ cmp_group, int Tc_cap) {
-  const long long e = static_cast<long long>(blockIdx.x) * kThreads + threadIdx.x;
+                                                          int32_t* __restrict__ cmp_group, int Tc_cap, int n0,
+                                                          int n1) {
+  const int bx = static_cast<int>(blockIdx.x);
   const int W = wl + wr + 1;
-  if (blockIdx.y == 0) {
-    if (e >= Tq || !(q_seg || q_pos || q_cmp_lo || q_cmp_nvis)) return;
-    const int i = static_cast<int>(e);
+  if (bx < n0) {
+    const int i = bx * kThreads + static_cast<int>(threadIdx.x);
+    if (i >= Tq) return;
     const int b = segment_of(cu_q, B, i);
     const int t = global_start + i;
     const int p = t - cu_kv[b];
@@ -66,18 +80,23 @@ __global__ __launch_bounds__(kThreads) void layout_kernel(const int32_t* __restr
     if (q_pos) q_pos[i] = p;
     if (q_cmp_lo) q_cmp_lo[i] = cu_cmp[b];
     if (q_cmp_nvis) q_cmp_nvis[i] = (p + 1) / r;
-  } else if (blockIdx.y == 1) {
-    if (win_idx == nullptr || e >= static_cast<long long>(Tq) * W) return;
-    const int i = static_cast<int>(e / W);
-    const int k = static_cast<int>(e - static_cast<long long>(i) * W);
-    const int b = segment_of(cu_q, B, i);
-    const int t = global_start + i;
-    const int lo = max(cu_kv[b], t - wl);
-    const int hi = min(cu_kv[b + 1] - 1, t + wr);
-    win_idx[e] = (lo + k <= hi) ? lo + k : -1;
+  } else if (bx < n0 + n1) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+#pragma unroll
+    for (int j = 0; j < kWinQueries / (kThreads / 64); ++j) {
+      const int i = (bx - n0) * kWinQueries + wave * (kWinQueries / (kThreads / 64)) + j;
+      if (i >= Tq) break;
+      const int b = segment_of_wave(cu_q, B, i);
+      const int t = global_start + i;
+      const int lo = max(cu_kv[b], t - wl);
+      const int hi = min(cu_kv[b + 1] - 1, t + wr);
+      int32_t* row = win_idx + static_cast<long long>(i) * W;
+      for (int k = lane; k < W; k += 64) row[k] = (lo + k <= hi) ? lo + k : -1;
+    }
   } else {
-    if (cmp_group == nullptr || e >= Tc_cap) return;
-    const int c = static_cast<int>(e);
+    const int c = (bx - n0 - n1) * kThreads + static_cast<int>(threadIdx.x);
+    if (c >= Tc_cap) return;
     if (c >= cu_cmp[B]) return;  // rows past the true count stay untouched
     const int b = segment_of(cu_cmp, B, c);
     cmp_group[c] = c - cu_cmp[b];
@@ -92,18 +111,16 @@ hipError_t launch_build_indices(const int32_t* cu_q, const int32_t* cu_kv, int B
                                 int32_t* q_cmp_nvis, int32_t* cmp_group, int Tc_cap, hipStream_t s) {
   (void)Tkv;
   hipLaunchKernelGGL(segment_scan_kernel, dim3(1), dim3(kThreads), 0, s, cu_kv, B, r, cu_cmp, residual);
-  const long long W = static_cast<long long>(wl) + wr + 1;
-  const long long n0 = (q_seg || q_pos || q_cmp_lo || q_cmp_nvis) ? Tq : 0;
-  const long long n1 = win_idx ? Tq * W : 0;
-  const long long n2 = cmp_group ? Tc_cap : 0;
-  const long long nmax = n0 > n1 ? (n0 > n2 ? n0 : n2) : (n1 > n2 ? n1 : n2);
-  if (nmax > 0) {
-    const unsigned gx = static_cast<unsigned>((nmax + kThreads - 1) / kThreads);
-    hipLaunchKernelGGL(layout_kernel, dim3(gx, 3), dim3(kThreads), 0, s, cu_q, cu_kv, cu_cmp, B, Tq,
-                       global_start, r, wl, wr, n0 ? q_seg : nullptr, n0 ? q_pos : nullptr,
-                       n1 ? win_idx : nullptr, n0 ? q_cmp_lo : nullptr, n0 ? q_cmp_nvis : nullptr,
-                       n2 ? cmp_group : nullptr, n2 ? Tc_cap : 0);
-  }
+  const bool tables = q_seg || q_pos || q_cmp_lo || q_cmp_nvis;
+  const long long n0 = tables ? (static_cast<long long>(Tq) + kThreads - 1) / kThreads : 0;
+  const long long n1 = win_idx ? (static_cast<long long>(Tq) + kWinQueries - 1) / kWinQueries : 0;
+  const long long n2 = cmp_group ? (static_cast<long long>(Tc_cap) + kThreads - 1) / kThreads : 0;
+  const long long nb = n0 + n1 + n2;
+  if (nb > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (nb > 0)
+    hipLaunchKernelGGL(layout_kernel, dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, s, cu_q, cu_kv, cu_cmp, B,
+                       Tq, global_start, r, wl, wr, q_seg, q_pos, win_idx, q_cmp_lo, q_cmp_nvis, cmp_group,
+                       n2 ? Tc_cap : 0, static_cast<int>(n0), static_cast<int>(n1));
   return hipGetLastError();
 }
 
