@@ -365,30 +365,30 @@ hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp
   const bool pair = cap >= 2048 && 2 * static_cast<size_t>(cap) * 4 <= 64 * 1024;
   if (mfma && !pair) {
     auto k = indexer_topk_kernel<1, uint16_t>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(lds));
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
                        static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r,
                        cap, topk, idx, score);
   } else if (mfma) {
     auto k = indexer_topk_pair_kernel;
     const size_t lds2 = 2 * static_cast<size_t>(cap) * 4;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(lds2));
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds2); e != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k, dim3((Tq + 1) / 2), block, lds2, s, static_cast<const uint16_t*>(q_I),
                        static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(k_cmp), cu_q, cu_kv, cu_cmp, B,
                        global_start, r, cap, topk, Tq, idx, score);
   } else if (dtype == 1) {
     auto k = indexer_topk_kernel<0, uint16_t>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(lds));
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
                        static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r,
                        cap, topk, idx, score);
   } else {
     auto k = indexer_topk_kernel<0, float>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(lds));
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const float*>(q_I), static_cast<const float*>(w),
                        static_cast<const float*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r, cap,
                        topk, idx, score);

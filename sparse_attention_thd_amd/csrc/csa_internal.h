@@ -6,6 +6,12 @@
 
 namespace csa {
 
+// Let kernel `k` take `bytes` of dynamic LDS (beyond the default limit); the launchers
+// return this call's error instead of launching when it fails.
+inline hipError_t allow_dynamic_lds(const void* k, size_t bytes) {
+  return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
 hipError_t launch_build_indices(const int32_t* cu_q, const int32_t* cu_kv, int B, int Tq, int Tkv,
                                 int global_start, int r, int wl, int wr, int32_t* q_seg, int32_t* q_pos,
                                 int32_t* win_idx, int32_t* cu_cmp, int32_t* residual, int32_t* q_cmp_lo,

@@ -487,16 +487,16 @@ hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_
   const size_t lds = (static_cast<size_t>(H) * d + d + 4 * static_cast<size_t>(H)) * sizeof(float);
   if (dtype == 1) {
     auto k = mla_fwd_generic_kernel<uint16_t>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(lds));
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k, dim3(Tq), dim3(kThreads), lds, s, static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, H, d,
                        cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale, static_cast<uint16_t*>(out),
                        lse);
   } else {
     auto k = mla_fwd_generic_kernel<float>;
-    hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                        static_cast<int>(lds));
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
+      return e;
     hipLaunchKernelGGL(k, dim3(Tq), dim3(kThreads), lds, s, static_cast<const float*>(q),
                        static_cast<const float*>(ori_kv), static_cast<const float*>(cmp_kv), cmp_idx, topk, H, d, cu_q,
                        cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale, static_cast<float*>(out), lse);
