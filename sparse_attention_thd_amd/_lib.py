@@ -68,7 +68,10 @@ def _check(code: int) -> None:
         raise CsaError(code, LIB.csa_last_error().decode())
 
 
-def _ptr(t, name, dtype=None, optional=False):
+def _ptr(t, name, dtype=None, optional=False, need=0):
+    """Device pointer of `t` after checking device, layout, dtype and that it holds at
+    least `need` elements (the extent the call's size arguments give it), so that a
+    short tensor is refused here instead of being read or written past its end."""
     if t is None:
         if optional:
             return None
@@ -81,6 +84,8 @@ def _ptr(t, name, dtype=None, optional=False):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {need}")
     return t.data_ptr()
 
 
@@ -110,30 +115,35 @@ def csa_build_indices(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, cmp
                       ori_win_right, q_seg, q_pos, win_idx, cu_seqlens_cmp, cmp_residual, q_cmp_lo, q_cmp_nvis,
                       cmp_group, Tc_cap, stream=None):
     i32 = torch.int32
+    W = ori_win_left + ori_win_right + 1
     _check(LIB.csa_build_indices(
-        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32), B, Tq, Tkv,
-        global_start, cmp_ratio, ori_win_left, ori_win_right,
-        _ptr(q_seg, "q_seg", i32, True), _ptr(q_pos, "q_pos", i32, True), _ptr(win_idx, "win_idx", i32, True),
-        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), _ptr(cmp_residual, "cmp_residual", i32),
-        _ptr(q_cmp_lo, "q_cmp_lo", i32, True), _ptr(q_cmp_nvis, "q_cmp_nvis", i32, True),
-        _ptr(cmp_group, "cmp_group", i32, True), Tc_cap, _stream(stream)))
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+        B, Tq, Tkv, global_start, cmp_ratio, ori_win_left, ori_win_right,
+        _ptr(q_seg, "q_seg", i32, True, Tq), _ptr(q_pos, "q_pos", i32, True, Tq),
+        _ptr(win_idx, "win_idx", i32, True, Tq * W),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1), _ptr(cmp_residual, "cmp_residual", i32, need=B),
+        _ptr(q_cmp_lo, "q_cmp_lo", i32, True, Tq), _ptr(q_cmp_nvis, "q_cmp_nvis", i32, True, Tq),
+        _ptr(cmp_group, "cmp_group", i32, True, Tc_cap), Tc_cap, _stream(stream)))
 
 
 def csa_compress(x, Tkv, d, cu_seqlens_kv, cu_seqlens_cmp, B, cmp_ratio, x_cmp, Tc_cap, stream=None):
     i32 = torch.int32
-    _check(LIB.csa_compress(_ptr(x, "x"), Tkv, d, _dtype_code(x), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-                            _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, cmp_ratio,
-                            _ptr(x_cmp, "x_cmp", x.dtype), Tc_cap, _stream(stream)))
+    _check(LIB.csa_compress(_ptr(x, "x", need=Tkv * d), Tkv, d, _dtype_code(x),
+                            _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+                            _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1), B, cmp_ratio,
+                            _ptr(x_cmp, "x_cmp", x.dtype, need=Tc_cap * d), Tc_cap, _stream(stream)))
 
 
 def csa_compress_learned(x, Tkv, D, wkv, wgate, ape, hd, overlap, cu_seqlens_kv, cu_seqlens_cmp, B, cmp_ratio,
                          x_cmp, Tc_cap, stream=None):
     i32 = torch.int32
-    _check(LIB.csa_compress_learned(_ptr(x, "x"), Tkv, D, _dtype_code(x), _ptr(wkv, "wkv", x.dtype),
-                                    _ptr(wgate, "wgate", x.dtype), _ptr(ape, "ape", torch.float32), hd,
-                                    1 if overlap else 0, _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-                                    _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, cmp_ratio,
-                                    _ptr(x_cmp, "x_cmp", x.dtype), Tc_cap, _stream(stream)))
+    C = (2 if overlap else 1) * hd
+    _check(LIB.csa_compress_learned(_ptr(x, "x", need=Tkv * D), Tkv, D, _dtype_code(x),
+                                    _ptr(wkv, "wkv", x.dtype, need=C * D), _ptr(wgate, "wgate", x.dtype, need=C * D),
+                                    _ptr(ape, "ape", torch.float32, need=cmp_ratio * C), hd, 1 if overlap else 0,
+                                    _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+                                    _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1), B, cmp_ratio,
+                                    _ptr(x_cmp, "x_cmp", x.dtype, need=Tc_cap * hd), Tc_cap, _stream(stream)))
 
 
 def csa_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
@@ -141,10 +151,11 @@ def csa_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, cu_seqlens_q, cu_seqlens_kv,
     i32 = torch.int32
     dt = q_I.dtype
     _check(LIB.csa_indexer_topk(
-        _ptr(q_I, "q_I"), _ptr(w, "w", dt), _ptr(k_I_cmp, "k_I_cmp", dt), Tq, H_I, d_I, _dtype_code(q_I),
-        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, global_start, cmp_ratio, max_seqlen_kv, topk,
-        _ptr(topk_idx, "topk_idx", i32), _ptr(topk_score, "topk_score", torch.float32, True), _stream(stream)))
+        _ptr(q_I, "q_I", need=Tq * H_I * d_I), _ptr(w, "w", dt, need=Tq * H_I), _ptr(k_I_cmp, "k_I_cmp", dt), Tq,
+        H_I, d_I, _dtype_code(q_I), _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1),
+        _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1), _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1),
+        B, global_start, cmp_ratio, max_seqlen_kv, topk, _ptr(topk_idx, "topk_idx", i32, need=Tq * topk),
+        _ptr(topk_score, "topk_score", torch.float32, True, Tq * topk), _stream(stream)))
 
 
 def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, H, d, cu_seqlens_q, cu_seqlens_kv,
@@ -153,12 +164,12 @@ def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, H, d, cu_seqle
     i32 = torch.int32
     dt = q.dtype
     _check(LIB.csa_sparse_mla_fwd(
-        _ptr(q, "q"), _ptr(ori_kv, "ori_kv", dt), _ptr(cmp_kv, "cmp_kv", dt, True),
-        _ptr(cmp_idx, "cmp_idx", i32, True), topk, Tq, Tkv, H, d, _dtype_code(q),
-        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True), B, global_start, cmp_ratio, ori_win_left,
-        ori_win_right, _ptr(sinks, "sinks", torch.float32, True), float(softmax_scale), _ptr(out, "out", dt),
-        _ptr(lse, "lse", torch.float32, True), _stream(stream)))
+        _ptr(q, "q", need=Tq * H * d), _ptr(ori_kv, "ori_kv", dt, need=Tkv * d), _ptr(cmp_kv, "cmp_kv", dt, True),
+        _ptr(cmp_idx, "cmp_idx", i32, True, Tq * topk), topk, Tq, Tkv, H, d, _dtype_code(q),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True, B + 1), B, global_start, cmp_ratio, ori_win_left,
+        ori_win_right, _ptr(sinks, "sinks", torch.float32, True, H), float(softmax_scale),
+        _ptr(out, "out", dt, need=Tq * H * d), _ptr(lse, "lse", torch.float32, True, Tq * H), _stream(stream)))
 
 
 def csa_sparse_mla_bwd_workspace_bytes(Tq, ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv,
@@ -178,16 +189,18 @@ def csa_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_s
     i32, f32 = torch.int32, torch.float32
     dt = q.dtype
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nq, W = Tq * H * d, ori_win_left + ori_win_right + 1
     _check(LIB.csa_sparse_mla_bwd(
-        _ptr(q, "q"), _ptr(ori_kv, "ori_kv", dt), _ptr(cmp_kv, "cmp_kv", dt, True),
-        _ptr(cmp_idx, "cmp_idx", i32, True), topk, Tq, Tkv, Tc, H, d, _dtype_code(q),
-        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True), B, global_start, cmp_ratio, ori_win_left, ori_win_right,
-        max_seqlen_kv, _ptr(sinks, "sinks", f32, True), float(softmax_scale), _ptr(out, "out", dt),
-        _ptr(lse, "lse", f32), _ptr(dout, "dout", dt), _ptr(dq, "dq", dt), _ptr(d_ori_kv, "d_ori_kv", f32),
-        _ptr(d_cmp_kv, "d_cmp_kv", f32, True), _ptr(d_sinks, "d_sinks", f32, True), _ptr(ori_l1, "ori_l1", f32, True),
-        _ptr(cmp_l1, "cmp_l1", f32, True), cmp_slots, _ptr(workspace, "workspace", optional=True), ws_bytes,
-        _stream(stream)))
+        _ptr(q, "q", need=nq), _ptr(ori_kv, "ori_kv", dt, need=Tkv * d), _ptr(cmp_kv, "cmp_kv", dt, True, Tc * d),
+        _ptr(cmp_idx, "cmp_idx", i32, True, Tq * topk), topk, Tq, Tkv, Tc, H, d, _dtype_code(q),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True, B + 1), B, global_start, cmp_ratio, ori_win_left,
+        ori_win_right, max_seqlen_kv, _ptr(sinks, "sinks", f32, True, H), float(softmax_scale),
+        _ptr(out, "out", dt, need=nq), _ptr(lse, "lse", f32, need=Tq * H), _ptr(dout, "dout", dt, need=nq),
+        _ptr(dq, "dq", dt, need=nq), _ptr(d_ori_kv, "d_ori_kv", f32, need=Tkv * d),
+        _ptr(d_cmp_kv, "d_cmp_kv", f32, True, Tc * d), _ptr(d_sinks, "d_sinks", f32, True, H),
+        _ptr(ori_l1, "ori_l1", f32, True, Tq * W), _ptr(cmp_l1, "cmp_l1", f32, True, Tq * cmp_slots), cmp_slots,
+        _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
 
 
 def csa_indexer_kl_grad_workspace_bytes(Tq, topk, max_seqlen_kv, cmp_ratio):
@@ -203,16 +216,19 @@ def csa_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, H_I, d_
     i32, f32 = torch.int32, torch.float32
     dt = q_I.dtype
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    nq = Tq * H_I * d_I
     _check(LIB.csa_indexer_kl_grad(
-        _ptr(q_I, "q_I"), _ptr(w, "w", dt), _ptr(k_I_cmp, "k_I_cmp", dt, True), _ptr(cmp_idx, "cmp_idx", i32),
-        _ptr(attn_l1, "attn_l1", f32), topk, Tq, Tc, H_I, d_I, _dtype_code(q_I),
-        _ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32), B, global_start, cmp_ratio, max_seqlen_kv, float(loss_scale),
-        _ptr(d_q_I, "d_q_I", dt), _ptr(d_w, "d_w", f32), _ptr(d_k_I_cmp, "d_k_I_cmp", f32, True),
-        _ptr(loss, "loss", f32, True), _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
+        _ptr(q_I, "q_I", need=nq), _ptr(w, "w", dt, need=Tq * H_I), _ptr(k_I_cmp, "k_I_cmp", dt, True, Tc * d_I),
+        _ptr(cmp_idx, "cmp_idx", i32, need=Tq * topk), _ptr(attn_l1, "attn_l1", f32, need=Tq * topk), topk, Tq, Tc,
+        H_I, d_I, _dtype_code(q_I), _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1),
+        _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1), _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1),
+        B, global_start, cmp_ratio, max_seqlen_kv, float(loss_scale), _ptr(d_q_I, "d_q_I", dt, need=nq),
+        _ptr(d_w, "d_w", f32, need=Tq * H_I), _ptr(d_k_I_cmp, "d_k_I_cmp", f32, True, Tc * d_I),
+        _ptr(loss, "loss", f32, True, Tq), _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
 
 
 def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, stream=None):
     i32 = torch.int32
-    _check(LIB.csa_validate_layout(_ptr(cu_seqlens_q, "cu_seqlens_q", i32), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32),
-                                   B, Tq, Tkv, global_start, max_seqlen_kv, _stream(stream)))
+    _check(LIB.csa_validate_layout(_ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1),
+                                   _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1), B, Tq, Tkv, global_start,
+                                   max_seqlen_kv, _stream(stream)))

@@ -273,3 +273,32 @@ def test_validate_layout_on_device():
         s.csa_validate_layout(cq, ck, p.B, p.Tq, p.Tkv, p.global_start + 1, p.max_seqlen_kv)
     with pytest.raises(s.CsaError):
         s.csa_validate_layout(cq, ck, p.B, p.Tq, p.Tkv, p.global_start, p.max_seqlen_kv - 1)
+
+
+def test_binding_refuses_short_tensors():
+    """A tensor holding fewer elements than the call's sizes give it is refused by the
+    binding before anything is launched."""
+    import sparse_attention_thd_amd as s
+    print("[case] short tensors -> ValueError before any launch", flush=True)
+    bf, i32 = torch.bfloat16, torch.int32
+    cu = torch.tensor([0, 64], dtype=i32, device="cuda")
+    Tq, H, d = 64, 64, 512
+    q = torch.zeros((Tq, H, d), dtype=bf, device="cuda")
+    kv = torch.zeros((Tq, d), dtype=bf, device="cuda")
+    out = torch.zeros((Tq, H, d), dtype=bf, device="cuda")
+    with pytest.raises(ValueError, match="q holds"):
+        s.csa_sparse_mla_fwd(q.view(-1)[:-1], kv, None, None, 0, Tq, Tq, H, d, cu, cu, None, 1, 0, 4, 127, 0, None,
+                             0.04, out)
+    with pytest.raises(ValueError, match="out holds"):
+        s.csa_sparse_mla_fwd(q, kv, None, None, 0, Tq, Tq, H, d, cu, cu, None, 1, 0, 4, 127, 0, None, 0.04,
+                             out.view(-1)[: Tq * H * d - d])
+    with pytest.raises(ValueError, match="cu_seqlens_kv holds"):
+        s.csa_sparse_mla_fwd(q, kv, None, None, 0, Tq, Tq, H, d, cu, cu[:1], None, 1, 0, 4, 127, 0, None, 0.04, out)
+    qI = torch.zeros((Tq, 64, 128), dtype=bf, device="cuda")
+    w = torch.zeros((Tq, 64), dtype=bf, device="cuda")
+    kI = torch.zeros((16, 128), dtype=bf, device="cuda")
+    cu_cmp = torch.tensor([0, 16], dtype=i32, device="cuda")
+    idx = torch.zeros((Tq, 8), dtype=i32, device="cuda")
+    with pytest.raises(ValueError, match="topk_idx holds"):
+        s.csa_indexer_topk(qI, w, kI, Tq, 64, 128, cu, cu, cu_cmp, 1, 0, 4, 64, 16, idx)
+    torch.cuda.synchronize()
