@@ -44,6 +44,10 @@ def _small(name):
         return pack_from_lengths("pair_long", [8301, 5, 2, 777], seed=24)
     if name == "topk1024":     # top-k above 512: the larger kernel instances, ~500 selecting queries
         return pack_from_lengths("topk1024", [4600, 300], seed=22, topk=1024)
+    if name == "max_limits":   # the largest candidate list (32768 = 131072 / r) and top-k (2048) the calls accept
+        return pack_from_lengths("max_limits", [131072], seed=25, topk=2048, q_rows=(131072 - 48, 131072))
+    if name == "wide_window":  # 1024 window slots per query (32 window tiles)
+        return pack_from_lengths("wide_window", [3000, 700], seed=26, ori_win_left=1023, topk=64)
     if name == "generic_f32":
         return pack_from_lengths("generic_f32", [5, 77, 140], seed=11, dtype="f32", H=4, d=64, H_I=2, d_I=32,
                                  ori_win_left=15, topk=8, q_scale=1.0, kv_scale=1.0, w_scale=2 ** -0.5,
@@ -56,7 +60,7 @@ def _small(name):
 
 FULL = ["tiny", "single4k", "pack16k", "hca32k", "cp32k", "stress"]
 SMALL = ["edges", "select16", "long", "short_only", "hca_small", "cp_small", "win_right", "no_compress",
-         "many_segs", "topk1024", "pair_long", "generic_f32", "generic_bf16"]
+         "many_segs", "topk1024", "pair_long", "max_limits", "wide_window", "generic_f32", "generic_bf16"]
 ALL = SMALL + FULL
 
 _cache = {}
