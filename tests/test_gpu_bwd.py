@@ -56,6 +56,8 @@ def _small(name):
         return pack_from_lengths("stress_small", [900], seed=14, topk=32, q_scale=1.0, kv_scale=1.0)
     if name == "topk1024":  # the top-k > 512 instances (up to 650 kept rows per query)
         return pack_from_lengths("topk1024", [2600, 150], seed=23, topk=1024)
+    if name == "max_limits":  # the largest candidate list (32768) and top-k (2048) the calls accept
+        return pack_from_lengths("max_limits", [131072], seed=25, topk=2048, q_rows=(131072 - 48, 131072))
     if name == "no_sinks":
         return dataclasses.replace(pack_from_lengths("no_sinks", [400, 90], seed=15, topk=32), sinks=None)
     raise KeyError(name)
@@ -126,7 +128,7 @@ def _oracle(pack, tabs, plan, dout, attend_all, slots, queries=None):
 
 
 SMALL = ["select16", "edges", "long", "short_only", "hca_small", "cp_small", "win_right", "no_compress",
-         "many_segs", "stress_small", "no_sinks", "topk1024"]
+         "many_segs", "stress_small", "no_sinks", "topk1024", "max_limits"]
 
 
 @pytest.mark.parametrize("name", SMALL)

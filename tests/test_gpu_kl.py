@@ -45,6 +45,8 @@ def _pack(name):
                                  topk=32)
     if name == "topk1024":  # the top-k > 512 instance (up to 650 kept rows per query)
         return pack_from_lengths("topk1024", [2600, 150], seed=23, topk=1024)
+    if name == "max_limits":  # the largest candidate list (32768) and top-k (2048) the calls accept
+        return pack_from_lengths("max_limits", [131072], seed=25, topk=2048, q_rows=(131072 - 48, 131072))
     raise KeyError(name)
 
 
@@ -129,7 +131,7 @@ def _check(pack, plan, p, scale, queries=None):
     return got
 
 
-@pytest.mark.parametrize("name", ["select16", "long", "edges", "many_segs", "cp_small", "topk1024"])
+@pytest.mark.parametrize("name", ["select16", "long", "edges", "many_segs", "cp_small", "topk1024", "max_limits"])
 def test_kl_grad_matches_oracle(name):
     pack = _pack(name)
     print(f"\n[case] {name}: Tq={pack.Tq} -> forward on GPU", flush=True)
