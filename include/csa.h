@@ -201,7 +201,8 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
  *   natural log of the full denominator in the scaled-logit domain.
  * Errors: EINVAL for NULL q/ori_kv/out/cu_seqlens*, cmp_idx without cmp_kv,
  * topk < 1 with cmp_idx, B < 1, Tq < 0, a window side < 0, cmp_ratio < 1,
- * global_start + Tq > Tkv; EUNSUPPORTED for shapes other than (H, d) = (64, 512)
+ * global_start + Tq > Tkv, softmax_scale not positive and finite; EUNSUPPORTED for
+ * shapes other than (H, d) = (64, 512)
  * bf16 or H * d <= 8192 with d % 8 == 0, or topk > 2048.
  */
 int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,

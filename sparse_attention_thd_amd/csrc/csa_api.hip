@@ -1,6 +1,7 @@
 // C ABI of libcsa: host-side argument checks, then kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -144,6 +145,9 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
   if (B < 1 || Tq < 0 || Tkv < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0)
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: invalid size or parameter");
   if (ori_win_left < 0 || ori_win_right < 0) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: window sides must be >= 0");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CSA_EINVAL, "csa_sparse_mla_fwd: softmax_scale (%g) must be positive and finite",
+                static_cast<double>(softmax_scale));
   if (static_cast<long long>(global_start) + Tq > Tkv)
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: global_start + Tq exceeds Tkv");
   if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: unknown dtype %d", dtype);

@@ -272,17 +272,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
 
-    // ---- online softmax; this lane holds keys kpi(4g+j) and 16+kpi(4g+j) of head `head`
-    float z[8];
-    float tmax = -__builtin_huge_valf();
+    // ---- online softmax; this lane holds keys kpi(4g+j) and 16+kpi(4g+j) of head `head`.
+    // Only the last tile can reach past the key list; its missing keys get -inf.  The
+    // scale is positive (checked by the caller), so the tile maximum is taken on the raw
+    // scores and scaled once, and each exponent is one fma.
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    if ((t + 1) * kNT > nkeys) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k0 = t * kNT + kpi(4 * g + j);
-      z[j] = (k0 < nkeys) ? s0[j] * scale_log2 : -__builtin_huge_valf();
-      z[4 + j] = (k0 + 16 < nkeys) ? s1[j] * scale_log2 : -__builtin_huge_valf();
-      tmax = fmaxf(tmax, fmaxf(z[j], z[4 + j]));
+      for (int j = 0; j < 4; ++j) {
+        const int k0 = t * kNT + kpi(4 * g + j);
+        sv[j] = (k0 < nkeys) ? sv[j] : -__builtin_huge_valf();
+        sv[4 + j] = (k0 + 16 < nkeys) ? sv[4 + j] : -__builtin_huge_valf();
+      }
     }
-    tmax = quad_max(tmax);
+    float smax = fmaxf(sv[0], sv[4]);
+#pragma unroll
+    for (int j = 1; j < 4; ++j) smax = fmaxf(smax, fmaxf(sv[j], sv[4 + j]));
+    const float tmax = quad_max(smax) * scale_log2;
     // Lazy rescale: keep a stale maximum while the tile stays within 2^8 of it.
     const bool rescale = __any(tmax > m_run + 8.f);
     float alpha = 1.f;
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     bf16x8 pb;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = __builtin_amdgcn_exp2f(z[j] - m_run);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], scale_log2, -m_run));
       l_run += p;
       pb[j] = static_cast<__bf16>(p);
     }

@@ -126,7 +126,9 @@ def _mla(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), EINVAL), (dict(out=None), EINVAL), (dict(ckv=None), EINVAL), (dict(topk=0), EINVAL),
     (dict(ckv=FAKE, cu_cmp=None), EINVAL), (dict(B=0), EINVAL), (dict(gs=1), EINVAL), (dict(wl=-1), EINVAL),
-    (dict(dtype=5), EINVAL), (dict(topk=4096), EUNSUP), (dict(H=128), EUNSUP), (dict(H=64, d=256), EUNSUP),
+    (dict(dtype=5), EINVAL), (dict(scale=0.0), EINVAL), (dict(scale=-0.04), EINVAL),
+    (dict(scale=float("inf")), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(topk=4096), EUNSUP),
+    (dict(H=128), EUNSUP), (dict(H=64, d=256), EUNSUP),
 ])
 def test_sparse_mla_rejects(kw, code):
     assert _mla(**kw) == code
