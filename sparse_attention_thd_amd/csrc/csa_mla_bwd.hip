@@ -292,8 +292,10 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
       float l0 = 0.f, l1 = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pa = v0 ? exp2f(s0[j] * scale_log2 - lse2[j]) : 0.f;
-        const float pb = v1 ? exp2f(s1[j] * scale_log2 - lse2[j]) : 0.f;
+        // v_exp_f32 directly: exponents are <= 0 here, and results below 2^-126 (flushed
+        // to zero) are far under the bf16 rounding of P
+        const float pa = v0 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s0[j], scale_log2, -lse2[j])) : 0.f;
+        const float pb = v1 ? __builtin_amdgcn_exp2f(__builtin_fmaf(s1[j], scale_log2, -lse2[j])) : 0.f;
         P0[j] = static_cast<__bf16>(pa);
         P1[j] = static_cast<__bf16>(pb);
         S0[j] = static_cast<__bf16>(scale * pa * (p0[j] - Dq[j]));
