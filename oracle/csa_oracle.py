@@ -50,8 +50,9 @@ compressed rows, p^ the main attention's head-averaged probabilities at those
 slots renormalised to sum 1; gradients through I = sum_h w relu(<q_I, k>), with
 relu'(0) = 0.
 
-"parity unpinned": ``ori_win_right > 0`` (clamped at the segment end) has no
-independent pin; every other function is pinned in ``tests/test_oracle_pins.py``.
+Every function is pinned in ``tests/test_oracle_pins.py`` (and the backward, KL
+and learned-compressor pin files); a window with a right side (``ori_win_right > 0``,
+clamped at the segment end) is pinned against torch's masked attention per segment.
 """
 from __future__ import annotations
 

@@ -249,6 +249,27 @@ def test_mla_window_only_is_causal_varlen_attention(seed):
         np.testing.assert_allclose(out[s:e], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_mla_band_window_with_right_side_is_masked_attention(seed):
+    """A window with both sides, clamped to the query's segment: per segment, torch's
+    attention with an explicit band mask (keys outside the segment do not exist there)."""
+    rng = np.random.default_rng(450 + seed)
+    L = _rand_lengths(rng, 3, 1, 30)
+    wl, wr = int(rng.integers(0, 6)), int(rng.integers(1, 5))
+    cu, T, q, kv, _, tabs = _mla_case(rng, L, wl=wl, wr=wr, sink=False)
+    scale = 0.29
+    out, _ = oracle.sparse_mla_fwd(q, kv, None, None, tabs, None, scale, wl, wr, cu, 0)
+    for b in range(len(L)):
+        s, e = int(cu[b]), int(cu[b + 1])
+        pos = np.arange(e - s)
+        band = (pos[None, :] >= pos[:, None] - wl) & (pos[None, :] <= pos[:, None] + wr)  # [query, key]
+        qq = torch.from_numpy(q[s:e]).permute(1, 0, 2)
+        kk = torch.from_numpy(kv[s:e])[None].expand(qq.shape[0], -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, kk, attn_mask=torch.from_numpy(band),
+                                                               scale=scale)
+        np.testing.assert_allclose(out[s:e], ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
 @pytest.mark.parametrize("seed", range(3))
 def test_mla_sink_is_an_extra_zero_valued_logit(seed):
     rng = np.random.default_rng(500 + seed)
