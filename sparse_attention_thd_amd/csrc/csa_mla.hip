@@ -168,19 +168,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
   // Tile 0 is all window rows when the window has at least a tile of them; then it is
   // issued here, so its latency overlaps the wait for the cmp_idx row.
-  const bool early_tile0 = qk.nwin >= kNT;
-  if (early_tile0) {
-    const uint16_t* src = ori_kv + static_cast<long long>(qk.lo + 4 * (lane & 7) + wave) * 512;
-    const unsigned long long a = reinterpret_cast<unsigned long long>(src);
-    const uint32_t a_lo = static_cast<uint32_t>(a), a_hi = static_cast<uint32_t>(a >> 32);
+  // A tile that lies inside the window holds stream rows lo + 32 t + r, so every row
+  // address is wave-uniform: formed in scalar registers, no lane lookup.
+  auto issue_window_tile = [&](int t, int bf) {
+    const uint16_t* src = ori_kv + static_cast<long long>(qk.lo + t * kNT + wave) * 512;
 #pragma unroll
-    for (int pass = 0; pass < kNT / kWaves; ++pass) {
-      const unsigned long long base = (static_cast<unsigned long long>(__builtin_amdgcn_readlane(a_hi, pass)) << 32) |
-                                      static_cast<uint32_t>(__builtin_amdgcn_readlane(a_lo, pass));
-      row_to_lds(reinterpret_cast<const void*>(base), lane16,
-                 kt_base + static_cast<uint32_t>((pass * kWaves + wave) * kRowStride));
-    }
-  }
+    for (int pass = 0; pass < kNT / kWaves; ++pass)
+      row_to_lds(src + pass * kWaves * 512, lane16,
+                 kt_base + static_cast<uint32_t>(bf * kTileBytes + (pass * kWaves + wave) * kRowStride));
+  };
+  const bool early_tile0 = qk.nwin >= kNT;
+  if (early_tile0) issue_window_tile(0, 0);
   if (sparse) {
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) vals[ch] = (ch * kThreads + tid < topk) ? vals[ch] : -1;
@@ -196,6 +194,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // row.  Rows past the key list re-read a valid row; their
   // probabilities are exactly zero.
   auto issue = [&](int t, int bf) {
+    if ((t + 1) * kNT <= qk.nwin) {
+      issue_window_tile(t, bf);
+      return;
+    }
     const int p = lane & 7;
     int kidx = t * kNT + 4 * p + wave;
     kidx = (kidx < nkeys) ? kidx : 0;
