@@ -1,0 +1,70 @@
+"""GPU parity on seeded random layouts: segment lengths, window sides, top-k, ratio
+(indexer, attend-every-visible-row, or window only) and query slices are drawn per
+case, and the whole forward is checked against the fp64 oracle as in the fixed cases:
+indices and compression bit-exact, top-k sets outside the tie band, attention and
+log-sum-exp within the forward's tolerances on every query (the packs are small).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_support import LSE_ABS, assert_out_close, check_topk_row, cpu, host_view, oracle_attention, oracle_tables, \
+    run_pack
+from synth import pack_from_lengths
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+SEEDS = list(range(12))
+
+
+def _random_pack(seed):
+    rng = np.random.default_rng(9000 + seed)
+    nseg = int(rng.integers(1, 9))
+    lengths = [int(v) for v in rng.integers(1, 900, size=nseg)]
+    total = sum(lengths)
+    ratio = int(rng.choice([4, 4, 4, 8, 1]))
+    wl, wr = int(rng.integers(0, 200)), int(rng.choice([0, 0, 0, int(rng.integers(1, 6))]))
+    topk = int(rng.choice([1, 7, 32, 64]))
+    q_rows = kv_rows = None
+    if total > 8 and rng.random() < 0.4:   # a query slice of the stream with its prefix KV
+        a = int(rng.integers(0, total // 2))
+        b = int(rng.integers(a + 1, total + 1))
+        q_rows, kv_rows = (a, b), b
+    return pack_from_lengths(f"random{seed}", lengths, seed=seed, cmp_ratio=ratio, ori_win_left=wl,
+                             ori_win_right=wr, topk=topk, indexer=(ratio == 4), q_rows=q_rows, kv_rows=kv_rows)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_layout_matches_oracle(seed):
+    pack = _random_pack(seed)
+    print(f"[case] random{seed}: lengths={np.diff(pack.cu_seqlens_kv).tolist()} Tq={pack.Tq} gs={pack.global_start} "
+          f"r={pack.cmp_ratio} window=({pack.ori_win_left},{pack.ori_win_right}) topk={pack.topk}", flush=True)
+    plan = run_pack(pack)
+    tabs = oracle_tables(pack)
+    Tc = int(tabs["cu_seqlens_cmp"][-1])
+    for k in ("q_seg", "q_pos", "win_idx", "q_cmp_lo", "q_cmp_nvis", "cu_seqlens_cmp", "cmp_residual"):
+        np.testing.assert_array_equal(cpu(getattr(plan, k)), tabs[k], err_msg=k)
+    mode = oracle.layer_compress_mode(pack.cmp_ratio, Tc)
+    cmp_kv = None
+    if mode != oracle.NO_COMPRESS:
+        cmp_kv = oracle.round_to(oracle.compress(host_view(pack, "ori_kv"), pack.cu_seqlens_kv, pack.cmp_ratio),
+                                 pack.dtype)
+        np.testing.assert_array_equal(cpu(plan.cmp_kv)[:Tc].astype(np.float64), cmp_kv)
+    rows = None
+    if mode == oracle.INDEXER:
+        kc = oracle.round_to(oracle.compress(host_view(pack, "k_I"), pack.cu_seqlens_kv, pack.cmp_ratio), pack.dtype)
+        np.testing.assert_array_equal(cpu(plan.k_I_cmp)[:Tc].astype(np.float64), kc)
+        idx, qI, w = cpu(plan.topk_idx), host_view(pack, "q_I"), host_view(pack, "w")
+        for i in range(pack.Tq):
+            lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
+            s = oracle.indexer_scores(qI[i], w[i], kc[lo:lo + nv]) if nv else np.zeros(0)
+            check_topk_row(idx[i], lo, nv, s, pack.topk)
+        rows = idx
+    qs = list(range(pack.Tq))
+    out, lse = oracle_attention(pack, tabs, qs, cmp_kv, rows, mode)
+    print("   ", assert_out_close(cpu(plan.out), out), flush=True)
+    assert np.abs(cpu(plan.lse) - lse).max() <= LSE_ABS
