@@ -2,7 +2,8 @@
 (indexer, attend-every-visible-row, or window only) and query slices are drawn per
 case, and the whole forward is checked against the fp64 oracle as in the fixed cases:
 indices and compression bit-exact, top-k sets outside the tie band, attention and
-log-sum-exp within the forward's tolerances on every query (the packs are small).
+log-sum-exp within the forward's tolerances on every query (the packs are small);
+the first six layouts also run the sparse-MLA backward against the oracle backward.
 """
 from __future__ import annotations
 
@@ -68,3 +69,25 @@ def test_random_layout_matches_oracle(seed):
     out, lse = oracle_attention(pack, tabs, qs, cmp_kv, rows, mode)
     print("   ", assert_out_close(cpu(plan.out), out), flush=True)
     assert np.abs(cpu(plan.lse) - lse).max() <= LSE_ABS
+
+
+@pytest.mark.parametrize("seed", SEEDS[:6])
+def test_random_layout_backward_matches_oracle(seed):
+    """The sparse-MLA backward on the same random layouts: dq, row gradients, sink
+    gradient and the probability outputs against the oracle backward."""
+    from test_gpu_bwd import L1_ABS, _close, _oracle, _run_bwd
+    pack = _random_pack(seed)
+    print(f"[case] random{seed}: backward Tq={pack.Tq} r={pack.cmp_ratio} topk={pack.topk}", flush=True)
+    plan = run_pack(pack)
+    got, dout, attend_all, slots = _run_bwd(pack, plan, seed=300 + seed)
+    tabs = oracle_tables(pack)
+    ref = _oracle(pack, tabs, plan, dout, attend_all, slots)
+    _close(got["dq"], ref["dq"], "dq")
+    _close(got["d_ori_kv"], ref["d_ori_kv"], "d_ori_kv")
+    if ref["d_cmp_kv"] is not None:
+        tc = ref["d_cmp_kv"].shape[0]
+        _close(got["d_cmp_kv"][:tc], ref["d_cmp_kv"], "d_cmp_kv")
+    _close(got["d_sinks"], ref["d_sinks"], "d_sinks")
+    assert np.abs(got["ori_l1"] - ref["ori_l1"]).max() <= L1_ABS
+    if slots:
+        assert np.abs(got["cmp_l1"] - ref["cmp_l1"]).max() <= L1_ABS
