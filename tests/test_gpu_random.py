@@ -3,7 +3,8 @@
 case, and the whole forward is checked against the fp64 oracle as in the fixed cases:
 indices and compression bit-exact, top-k sets outside the tie band, attention and
 log-sum-exp within the forward's tolerances on every query (the packs are small);
-the first six layouts also run the sparse-MLA backward against the oracle backward.
+the first six layouts also run the sparse-MLA backward against the oracle backward,
+and the layouts drawn with the indexer run its KL-loss gradient against the oracle.
 """
 from __future__ import annotations
 
@@ -91,3 +92,17 @@ def test_random_layout_backward_matches_oracle(seed):
     assert np.abs(got["ori_l1"] - ref["ori_l1"]).max() <= L1_ABS
     if slots:
         assert np.abs(got["cmp_l1"] - ref["cmp_l1"]).max() <= L1_ABS
+
+
+INDEXER_SEEDS = [2, 3, 8, 9, 10, 11]  # the layouts above drawn with ratio 4 (checked in the test)
+
+
+@pytest.mark.parametrize("seed", INDEXER_SEEDS)
+def test_random_layout_kl_grad_matches_oracle(seed):
+    """The indexer KL gradient on the random layouts that run the indexer."""
+    from test_gpu_kl import _check, _targets
+    pack = _random_pack(seed)
+    assert pack.has_indexer and pack.cmp_ratio == 4
+    print(f"[case] random{seed}: KL gradient Tq={pack.Tq} topk={pack.topk}", flush=True)
+    plan = run_pack(pack)
+    _check(pack, plan, _targets(plan, 400 + seed), 1.0 / max(pack.Tq, 1))
