@@ -89,7 +89,8 @@ const char* csa_last_error(void);
  *   cmp_group  [Tc_cap]  segment-local group id c - cu_seqlens_cmp[b]
  * Every per-query / per-row output pointer may be NULL (not written).
  * Errors: EINVAL for NULL cu_seqlens_*, B < 1, Tq < 0, Tkv < 0, global_start < 0,
- * global_start + Tq > Tkv, cmp_ratio < 1, a window side < 0, Tc_cap < Tkv / r,
+ * global_start + Tq > Tkv, cmp_ratio < 1, a window side < 0 (or Tkv plus both
+ * sides >= 2^31), Tc_cap < Tkv / r,
  * or a NULL required output.
  */
 int csa_build_indices(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B,
@@ -200,7 +201,8 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
  *   out [Tq, H, d] (call dtype), lse [Tq, H] float32 (NULL = not written):
  *   natural log of the full denominator in the scaled-logit domain.
  * Errors: EINVAL for NULL q/ori_kv/out/cu_seqlens*, cmp_idx without cmp_kv,
- * topk < 1 with cmp_idx, B < 1, Tq < 0, a window side < 0, cmp_ratio < 1,
+ * topk < 1 with cmp_idx, B < 1, Tq < 0, a window side < 0 (or Tkv plus both sides
+ * >= 2^31), cmp_ratio < 1,
  * global_start + Tq > Tkv, softmax_scale not positive and finite; EUNSUPPORTED for
  * shapes other than (H, d) = (64, 512)
  * bf16 or H * d <= 8192 with d % 8 == 0, or topk > 2048.

@@ -42,6 +42,12 @@ const char* csa_version(void) { return "csa-gfx950 0.1.0"; }
 
 const char* csa_last_error(void) { return g_last_error.c_str(); }
 
+// Window sides: non-negative, and small enough that a stream row plus or minus a side
+// (and the slot count left + right + 1) stays within int32.
+static bool window_fits(int32_t wl, int32_t wr, int32_t Tkv) {
+  return wl >= 0 && wr >= 0 && static_cast<long long>(Tkv) + wl + wr + 1 <= 0x7fffffffLL;
+}
+
 int csa_build_indices(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B, int32_t Tq,
                       int32_t Tkv, int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left,
                       int32_t ori_win_right, int32_t* q_seg, int32_t* q_pos, int32_t* win_idx,
@@ -57,8 +63,8 @@ int csa_build_indices(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
     return fail(CSA_EINVAL, "csa_build_indices: global_start + Tq (%lld) exceeds Tkv (%d)",
                 static_cast<long long>(global_start) + Tq, Tkv);
   if (cmp_ratio < 1) return fail(CSA_EINVAL, "csa_build_indices: cmp_ratio must be >= 1");
-  if (ori_win_left < 0 || ori_win_right < 0)
-    return fail(CSA_EINVAL, "csa_build_indices: window sides must be >= 0");
+  if (!window_fits(ori_win_left, ori_win_right, Tkv))
+    return fail(CSA_EINVAL, "csa_build_indices: window sides must be >= 0 with Tkv + sides < 2^31");
   if (cmp_group && Tc_cap < Tkv / cmp_ratio)
     return fail(CSA_EINVAL, "csa_build_indices: Tc_cap (%d) < Tkv / cmp_ratio (%d)", Tc_cap, Tkv / cmp_ratio);
   return hip_status(csa::launch_build_indices(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, cmp_ratio,
@@ -144,7 +150,8 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
   if (cmp_idx && topk < 1) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: topk must be >= 1 with cmp_idx");
   if (B < 1 || Tq < 0 || Tkv < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0)
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: invalid size or parameter");
-  if (ori_win_left < 0 || ori_win_right < 0) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: window sides must be >= 0");
+  if (!window_fits(ori_win_left, ori_win_right, Tkv))
+    return fail(CSA_EINVAL, "csa_sparse_mla_fwd: window sides must be >= 0 with Tkv + sides < 2^31");
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: softmax_scale (%g) must be positive and finite",
                 static_cast<double>(softmax_scale));
@@ -181,7 +188,7 @@ static int bwd_nvis_cap(const void* cmp_kv, const int32_t* cmp_idx, int32_t max_
 int64_t csa_sparse_mla_bwd_workspace_bytes(int32_t Tq, int32_t ori_win_left, int32_t ori_win_right,
                                            const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
                                            int32_t max_seqlen_kv, int32_t cmp_ratio) {
-  if (Tq < 0 || ori_win_left < 0 || ori_win_right < 0 || cmp_ratio < 1 || max_seqlen_kv < 0) return -1;
+  if (Tq < 0 || !window_fits(ori_win_left, ori_win_right, 0) || cmp_ratio < 1 || max_seqlen_kv < 0) return -1;
   const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
   return static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap, bwd_nvis_cap(cmp_kv, cmp_idx, max_seqlen_kv,
                                                                                  cmp_ratio)));
@@ -206,7 +213,11 @@ int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, co
   if (B < 1 || Tq < 0 || Tkv < 0 || Tc < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0 ||
       max_seqlen_kv < 0 || cmp_slots < 0)
     return fail(CSA_EINVAL, "csa_sparse_mla_bwd: invalid size or parameter");
-  if (ori_win_left < 0 || ori_win_right < 0) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: window sides must be >= 0");
+  if (!window_fits(ori_win_left, ori_win_right, Tkv))
+    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: window sides must be >= 0 with Tkv + sides < 2^31");
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: softmax_scale (%g) must be positive and finite",
+                static_cast<double>(softmax_scale));
   if (static_cast<long long>(global_start) + Tq > Tkv)
     return fail(CSA_EINVAL, "csa_sparse_mla_bwd: global_start + Tq exceeds Tkv");
   if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: unknown dtype %d", dtype);

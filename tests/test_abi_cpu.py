@@ -54,6 +54,7 @@ def _bi(**kw):
     (dict(cu_q=None), EINVAL), (dict(cu_kv=None), EINVAL), (dict(cu_cmp=None), EINVAL), (dict(res=None), EINVAL),
     (dict(B=0), EINVAL), (dict(Tq=-1), EINVAL), (dict(Tq=5), EINVAL), (dict(gs=1), EINVAL),
     (dict(r=0), EINVAL), (dict(wl=-1), EINVAL), (dict(wr=-2), EINVAL), (dict(grp=FAKE, Tc_cap=0, r=2), EINVAL),
+    (dict(wl=2**31 - 4), EINVAL), (dict(wl=2**30, wr=2**30), EINVAL),
 ])
 def test_build_indices_rejects(kw, code):
     assert _bi(**kw) == code
@@ -127,6 +128,7 @@ def _mla(**kw):
     (dict(q=None), EINVAL), (dict(out=None), EINVAL), (dict(ckv=None), EINVAL), (dict(topk=0), EINVAL),
     (dict(ckv=FAKE, cu_cmp=None), EINVAL), (dict(B=0), EINVAL), (dict(gs=1), EINVAL), (dict(wl=-1), EINVAL),
     (dict(dtype=5), EINVAL), (dict(scale=0.0), EINVAL), (dict(scale=-0.04), EINVAL),
+    (dict(wl=2**31 - 8), EINVAL), (dict(wr=2**31 - 8), EINVAL),
     (dict(scale=float("inf")), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(topk=4096), EUNSUP),
     (dict(H=128), EUNSUP), (dict(H=64, d=256), EUNSUP),
 ])
@@ -147,7 +149,8 @@ def _mla_bwd(**kw):
     (dict(q=None), EINVAL), (dict(dout=None), EINVAL), (dict(lse=None), EINVAL), (dict(dq=None), EINVAL),
     (dict(ws=None), EINVAL), (dict(dkv=None), EINVAL), (dict(dcmp=None), EINVAL), (dict(dsinks=None), EINVAL),
     (dict(ckv=None), EINVAL), (dict(topk=0), EINVAL), (dict(cl1=FAKE, slots=0), EINVAL), (dict(B=0), EINVAL),
-    (dict(gs=1), EINVAL), (dict(wr=-1), EINVAL), (dict(ws_bytes=1024), EINVAL), (dict(topk=4096), EUNSUP),
+    (dict(gs=1), EINVAL), (dict(wr=-1), EINVAL), (dict(wl=2**31 - 8), EINVAL), (dict(scale=0.0), EINVAL),
+    (dict(scale=float("nan")), EINVAL), (dict(ws_bytes=1024), EINVAL), (dict(topk=4096), EUNSUP),
     (dict(H=16), EUNSUP), (dict(dtype=0), EUNSUP),
 ])
 def test_sparse_mla_bwd_rejects(kw, code):
@@ -165,6 +168,7 @@ def test_sparse_mla_bwd_workspace_size_formula():
     n_all = LIB.csa_sparse_mla_bwd_workspace_bytes(3, 127, 0, FAKE, None, 0, 1000, 4)  # attend-all: 128 + 250 keys
     assert n_all == total(3, 384 * 256 + 4 + 256)
     assert LIB.csa_sparse_mla_bwd_workspace_bytes(-1, 127, 0, None, None, 0, 0, 4) == -1
+    assert LIB.csa_sparse_mla_bwd_workspace_bytes(1, 2**31 - 1, 1, None, None, 0, 0, 4) == -1  # sides overflow int32
     # a window wider than the longest segment holds at most max_seqlen_kv keys
     n_wide = LIB.csa_sparse_mla_bwd_workspace_bytes(2, 100000, 0, None, None, 0, 300, 4)
     assert n_wide == total(2, 320 * 256 + 4 + 256)
