@@ -118,19 +118,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) vals[ch] = row[min(ch * kThreads + tid, topk - 1)];
   }
-  // B operand of S^T = K . Q^T.  Within MFMA step ks, k-slot 8g + j of lane group g
-  // stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 + 4*g + (j - 4): the same
-  // permutation the K fragments use, chosen so each half is one conflict-free 8-byte
-  // LDS read (a 16-byte ds_read_b128 of the same data is several times slower).
-  bf16x8 qf[16];
+  // The query's 64 q rows (64 KiB, contiguous) are staged through the idle tile buffers
+  // as whole 1 KiB rows, one global_load_lds_dwordx4 per row (wave w: heads 16w ..
+  // 16w + 15, padded rows), and read back as fragments once they have landed.
+  const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
+  const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
   {
-    const uint16_t* qrow = q + (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
+    const uint16_t* qsrc = q + (static_cast<long long>(i) * 64 + 16 * wave) * 512;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(qrow + 32 * ks);
-      const uint2 hi = *reinterpret_cast<const uint2*>(qrow + 32 * ks + 16);
-      qf[ks] = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-    }
+    for (int hh = 0; hh < 16; ++hh)
+      row_to_lds(qsrc + hh * 512, lane16, kt_base + static_cast<uint32_t>((16 * wave + hh) * kRowStride));
   }
   // segment of query row i: count segment starts <= i (one ballot per 64 segments)
   int count = __popcll(__ballot(cu0 <= i));
@@ -164,10 +161,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     qk.ncmp = 0;
     if (cmp_kv != nullptr && cmp_idx == nullptr) qk.ncmp = max(0, min((t_abs - seg_s + 1) / r, cmp_end - qk.cmp_base));
   }
-  const uint32_t kt_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kt)));
-  const uint32_t lane16 = static_cast<uint32_t>(lane) << 4;
-  // Tile 0 is all window rows when the window has at least a tile of them; then it is
-  // issued here, so its latency overlaps the wait for the cmp_idx row.
   // A tile that lies inside the window holds stream rows lo + 32 t + r, so every row
   // address is wave-uniform: formed in scalar registers, no lane lookup.
   auto issue_window_tile = [&](int t, int bf) {
@@ -177,8 +170,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       row_to_lds(src + pass * kWaves * 512, lane16,
                  kt_base + static_cast<uint32_t>(bf * kTileBytes + (pass * kWaves + wave) * kRowStride));
   };
-  const bool early_tile0 = qk.nwin >= kNT;
-  if (early_tile0) issue_window_tile(0, 0);
   if (sparse) {
 #pragma unroll
     for (int ch = 0; ch < NC; ++ch) vals[ch] = (ch * kThreads + tid < topk) ? vals[ch] : -1;
@@ -220,7 +211,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                  kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
     }
   };
-  if (ntiles > 0 && !early_tile0) issue(0, 0);
+  // q rows landed everywhere -> B operand of S^T = K . Q^T.  Within MFMA step ks, k-slot
+  // 8g + j of lane group g stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 +
+  // 4*g + (j - 4): the same permutation the K fragments use, so each half is one
+  // conflict-free 8-byte LDS read (rows 1040 bytes apart fall 4 banks apart).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  tile_barrier();
+  bf16x8 qf[16];
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks)
+    qf[ks] = kfrag(kt, head * kRowStride + 64 * ks + 8 * g, head * kRowStride + 64 * ks + 8 * g + 32);
+  lds_barrier();  // every wavefront has its q fragments: the tile buffers are free
+  if (ntiles > 0) issue(0, 0);
 
   // Drain here (tile 0 is needed first anyway) so that no compiler-placed wait for
   // these loads lands inside the tile loop, where it would also drain the prefetch.
