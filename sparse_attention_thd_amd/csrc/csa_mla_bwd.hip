@@ -216,12 +216,29 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
                  kt_base + static_cast<uint32_t>(bf * kTileBytes + rr * kRowStride));
     }
   };
+  // The query's 64 q rows (64 KiB, contiguous) arrive as whole 1 KiB rows in kv buffers
+  // 1 and 2 (idle until the loop's first barrier), one global_load_lds_dwordx4 per row
+  // (wavefront w8: rows 8 w8 .. 8 w8 + 7), issued before tile 0 so that vmcnt(4) covers
+  // them; the S wavefronts read their fragments from there.
+  {
+    const uint16_t* qsrc = q + (static_cast<long long>(i) * 64 + 8 * wave8) * 512;
+#pragma unroll
+    for (int hh = 0; hh < 8; ++hh)
+      row_to_lds(qsrc + hh * 512, lane16, kt_base + static_cast<uint32_t>(kTileBytes + (8 * wave8 + hh) * kRowStride));
+  }
   if (ntiles > 0) issue(0, 0);
+  if (ntiles > 0) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): only tile 0 may be in flight
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
+  tile_barrier();  // every wavefront's q rows have landed
 
   if (s_wave) {
     const long long qoff = (static_cast<long long>(i) * 64 + head) * 512 + 4 * g;
     bf16x8 qf[16], df[16];
-    load_qstyle(q + qoff, qf);
+    {
+      const unsigned char* qb = kt + kTileBytes + head * kRowStride + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) qf[ks] = kfrag(qb, 64 * ks, 64 * ks + 32);
+    }
     load_qstyle(dout + qoff, df);
     // D = dout . out of head 16 wave + n: each lane sums its 128 dims, then the quad
     float dsum = 0.f;
