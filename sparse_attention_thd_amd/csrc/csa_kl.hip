@@ -276,15 +276,27 @@ __global__ __launch_bounds__(kThreads) void kl_query_kernel(
   // d_w[head]: the lane quad holds disjoint rows
   dw = quad_sum(dw);
   if (g == 0) d_w[static_cast<long long>(i) * 64 + head] = dw;
-  // d_q^T column `head`, dims 16 db + 4 g + j
-  uint16_t* qout = d_q + (static_cast<long long>(i) * 64 + head) * 128 + 4 * g;
+  // d_q rows leave as whole rows: staged in the (now idle) K stage buffers as 64 rows of
+  // 256 bytes, 16-byte chunk c of row h at chunk c ^ (h & 15) (conflict-free writes),
+  // then stored 1 KiB per instruction.  A wavefront's rows are its own heads, so after
+  // the barrier that frees the buffers it reads back only what it wrote itself.
+  lds_barrier();
+  unsigned char* st = &kst[0][0];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < 8; ++db) {  // dims 16 db + 4 g + j of head `head`
     const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(dq[db][0])) |
                         (static_cast<uint32_t>(f32_to_bf16_bits(dq[db][1])) << 16);
     const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(dq[db][2])) |
                         (static_cast<uint32_t>(f32_to_bf16_bits(dq[db][3])) << 16);
-    *reinterpret_cast<uint2*>(qout + 16 * db) = make_uint2(w0, w1);
+    const int c = 2 * db + (g >> 1);
+    *reinterpret_cast<uint2*>(st + head * 256 + ((c ^ (head & 15)) << 4) + (g & 1) * 8) = make_uint2(w0, w1);
+  }
+  uint16_t* obase = d_q + (static_cast<long long>(i) * 64 + 16 * wave) * 128;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 4 * k + (lane >> 4), c = lane & 15;  // row 16 wave + r, chunk c
+    const uint4 v = *reinterpret_cast<const uint4*>(st + (16 * wave + r) * 256 + ((c ^ r) << 4));
+    *reinterpret_cast<uint4*>(obase + r * 128 + c * 8) = v;
   }
 }
 
