@@ -387,15 +387,30 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
       lds_barrier();  // the dS rows of the last tile
       dq_tile(ntiles - 1);
     }
-    // dq^T column (head 16 wave + n), dims 16 mb + 4 g + j: 8 bytes per lane and block
-    uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * wave + n) * 512 + 4 * g;
-#pragma unroll
-    for (int mb = 0; mb < 32; ++mb) {
+    // dq^T column (head 16 wave + n), dims 16 mb + 4 g + j.  The rows leave whole: this
+    // wavefront stages its 16 head rows (padded, conflict-free 8-byte writes) in a kv
+    // buffer nobody reads any more (not the last tile's; no load is in flight), then
+    // stores one 1 KiB row per instruction.  With no tile at all the q rows may still
+    // sit in buffers 1 and 2, so that case stores its (zero) rows directly.
+    auto pack = [&](int mb) {
       const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0])) |
                           (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1])) << 16);
       const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2])) |
                           (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3])) << 16);
-      *reinterpret_cast<uint2*>(qrow + 16 * mb) = make_uint2(w0, w1);
+      return make_uint2(w0, w1);
+    };
+    if (ntiles == 0) {
+      uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * wave + n) * 512 + 4 * g;
+#pragma unroll
+      for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<uint2*>(qrow + 16 * mb) = pack(mb);
+    } else {
+      unsigned char* st = kt + ((ntiles + (wave >> 1)) % 3) * kTileBytes + (16 * (wave & 1)) * kRowStride;
+#pragma unroll
+      for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<uint2*>(st + n * kRowStride + 32 * mb + 8 * g) = pack(mb);
+      uint16_t* obase = dq + (static_cast<long long>(i) * 64 + 16 * wave) * 512 + 8 * lane;
+#pragma unroll
+      for (int hh = 0; hh < 16; ++hh)
+        *reinterpret_cast<uint4*>(obase + hh * 512) = *reinterpret_cast<const uint4*>(st + hh * kRowStride + 16 * lane);
     }
   }
 }
