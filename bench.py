@@ -168,8 +168,9 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
     cmp_idx = plan.topk_idx
     topk = plan.topk if cmp_idx is not None else 0
     lse = torch.empty((pack.Tq, pack.H), dtype=torch.float32, device="cuda")
-    _lib.csa_sparse_mla_fwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx, topk, L.Tq, L.Tkv, plan.H, plan.d,
-                            L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r,
+    _lib.csa_sparse_mla_fwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx, topk, _lib.CSA_IDX_TOPK, L.Tq, L.Tkv,
+                            plan.Tc_cap if plan.cmp_kv is not None else 0, plan.H, plan.d, L.cu_seqlens_q,
+                            L.cu_seqlens_kv, plan.cu_seqlens_cmp, plan.cmp_residual, L.B, L.global_start, plan.r,
                             plan.wl, plan.wr, inputs["sinks"], plan.scale, plan.out, lse)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(1234)
@@ -290,6 +291,105 @@ def learned_bench(plan, pack, steps, warmup, D=4096):
     return res
 
 
+def time_forward(plan, inputs, steps, warmup):
+    """W untimed and K timed forward steps; per-phase HIP-event times (ms) on the launch
+    stream: the index build + both compressions, the indexer + top-k, the sparse MLA."""
+    import torch
+    from sparse_attention_thd_amd import _lib
+    L = plan.L
+
+    def front():
+        _lib.csa_build_indices(L.cu_seqlens_q, L.cu_seqlens_kv, L.B, L.Tq, L.Tkv, L.global_start, plan.r, plan.wl,
+                               plan.wr, plan.q_seg, plan.q_pos, plan.win_idx, plan.cu_seqlens_cmp, plan.cmp_residual,
+                               plan.q_cmp_lo, plan.q_cmp_nvis, plan.cmp_group, plan.Tc_cap)
+        if plan.cmp_kv is not None:
+            _lib.csa_compress(inputs["ori_kv"], L.Tkv, plan.d, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, plan.r,
+                              plan.cmp_kv, plan.Tc_cap)
+        if plan.topk_idx is not None:
+            _lib.csa_compress(inputs["k_I"], L.Tkv, plan.d_I, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, plan.r,
+                              plan.k_I_cmp, plan.Tc_cap)
+
+    def indexer():
+        if plan.topk_idx is not None:
+            _lib.csa_indexer_topk(inputs["q_I"], inputs["w"], plan.k_I_cmp, L.Tq, plan.Tc_cap, plan.H_I, plan.d_I,
+                                  L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, plan.cmp_residual, L.B,
+                                  L.global_start, plan.r, L.max_seqlen_kv, plan.topk, plan.topk_idx, None)
+
+    def mla():
+        cmp_idx = plan.topk_idx
+        _lib.csa_sparse_mla_fwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx,
+                                plan.topk if cmp_idx is not None else 0, _lib.CSA_IDX_TOPK, L.Tq, L.Tkv,
+                                plan.Tc_cap if plan.cmp_kv is not None else 0, plan.H, plan.d, L.cu_seqlens_q,
+                                L.cu_seqlens_kv, plan.cu_seqlens_cmp, plan.cmp_residual, L.B, L.global_start, plan.r,
+                                plan.wl, plan.wr, inputs["sinks"], plan.scale, plan.out, None)
+
+    for _ in range(warmup):
+        front(); indexer(); mla()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(E(), E(), E(), E()) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1, e2, e3 in ev:
+        e0.record(); front(); e1.record(); indexer(); e2.record(); mla(); e3.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    return {"front": np.array([a.elapsed_time(b) for a, b, _, _ in ev]),
+            "indexer": np.array([b.elapsed_time(c) for _, b, c, _ in ev]),
+            "mla": np.array([c.elapsed_time(d) for _, _, c, d in ev]),
+            "step": np.array([a.elapsed_time(d) for a, _, _, d in ev]), "wall": wall}
+
+
+def workload_bench(name, seed, steps, warmup):
+    """Throughput of the whole forward on another workload's layout, inputs drawn on the
+    device (same scales as the synthetic packs; the work counts depend only on the
+    layout).  The sparse MLA is reported against the bf16 MFMA peak and, by its
+    compulsory bytes (q and out of every query, every latent and compressed row once),
+    against HBM: with few attended rows per query (the ratio-128 pack) it is HBM-bound."""
+    import torch
+    from synth import workload_layout
+    from sparse_attention_thd_amd import CsaPlan, ThdLayout
+    lay = workload_layout(name, seed)
+    layout = ThdLayout.from_host(lay.cu_seqlens_q, lay.cu_seqlens_kv, lay.global_start)
+    plan = CsaPlan(layout, H=lay.H, d=lay.d, H_I=lay.H_I, d_I=lay.d_I, cmp_ratio=lay.cmp_ratio,
+                   ori_win_left=lay.ori_win_left, ori_win_right=lay.ori_win_right, topk=lay.topk,
+                   softmax_scale=lay.softmax_scale, dtype=torch.bfloat16)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1000 + seed)
+    rnd = lambda shape, sc: (torch.randn(shape, generator=gen, device="cuda") * sc).to(torch.bfloat16)
+    inputs = dict(q=rnd((lay.Tq, lay.H, lay.d), lay.q_scale), ori_kv=rnd((lay.Tkv, lay.d), lay.kv_scale),
+                  sinks=torch.randn(lay.H, generator=gen, device="cuda"))
+    if lay.indexer:
+        inputs.update(q_I=rnd((lay.Tq, lay.H_I, lay.d_I), 1.0), k_I=rnd((lay.Tkv, lay.d_I), 1.0),
+                      w=rnd((lay.Tq, lay.H_I), lay.w_scale))
+    torch.cuda.synchronize()
+    t = time_forward(plan, inputs, steps, warmup)
+
+    class P:  # the fields algorithmic_work reads
+        Tq, global_start, ori_win_left, ori_win_right, topk = lay.Tq, lay.global_start, lay.ori_win_left, \
+            lay.ori_win_right, lay.topk
+    nwin, ncmp, need = algorithmic_work(plan, P)
+    ms_step, mla_ms, idx_ms = float(t["step"].mean()), float(t["mla"].mean()), float(t["indexer"].mean())
+    mla_flops = 4.0 * lay.H * lay.d * (nwin + ncmp)
+    Tc = int(plan.cu_seqlens_cmp[-1].item())
+    hbm_bytes = lay.Tq * lay.H * lay.d * 2 * 2 + (lay.Tkv + Tc) * lay.d * 2
+    res = {"workload": f"{name}: {WORKLOAD_TEXT[name]}", "tokens": lay.Tq, "segments": lay.B, "steps": steps,
+           "warmup": warmup, "ms_per_step": ms_step, "tokens_per_s": lay.Tq / (ms_step / 1e3),
+           "phases_ms": {"indices+compress": float(t["front"].mean()), "indexer_topk": idx_ms, "sparse_mla": mla_ms},
+           "sparse_mla": {"attended_rows": nwin + ncmp, "rows_per_query": (nwin + ncmp) / max(lay.Tq, 1),
+                          "algorithmic_flops": mla_flops,
+                          "frac_of_bf16_peak": mla_flops / (mla_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "compulsory_hbm_bytes": hbm_bytes,
+                          "frac_of_hbm": hbm_bytes / (mla_ms / 1e3) / 1e9 / PEAK_HBM_GBS}}
+    if plan.topk_idx is not None:
+        idx_flops = 2.0 * lay.H_I * lay.d_I * need
+        res["indexer"] = {"needed_score_flops": idx_flops,
+                          "frac_of_bf16_peak": idx_flops / (idx_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+    del inputs, plan
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -303,6 +403,8 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=10)
     ap.add_argument("--no-kl", action="store_true", help="skip the indexer KL-loss gradient measurement")
     ap.add_argument("--no-learned", action="store_true", help="skip the learned compressor measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the forward on the other workloads (single4k, hca32k, cp32k)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -334,50 +436,8 @@ def main():
                   k_I=_dev(pack.k_I), w=_dev(pack.w))
     torch.cuda.synchronize()
 
-    # split the step so the sparse-MLA launch can be bracketed by events on the same stream
-    from sparse_attention_thd_amd import _lib
-    L = plan.L
-
-    def front():
-        _lib.csa_build_indices(L.cu_seqlens_q, L.cu_seqlens_kv, L.B, L.Tq, L.Tkv, L.global_start, plan.r, plan.wl,
-                               plan.wr, plan.q_seg, plan.q_pos, plan.win_idx, plan.cu_seqlens_cmp, plan.cmp_residual,
-                               plan.q_cmp_lo, plan.q_cmp_nvis, plan.cmp_group, plan.Tc_cap)
-        if plan.cmp_kv is not None:
-            _lib.csa_compress(inputs["ori_kv"], L.Tkv, plan.d, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, plan.r,
-                              plan.cmp_kv, plan.Tc_cap)
-        if plan.topk_idx is not None:
-            _lib.csa_compress(inputs["k_I"], L.Tkv, plan.d_I, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, plan.r,
-                              plan.k_I_cmp, plan.Tc_cap)
-
-    def indexer():
-        if plan.topk_idx is not None:
-            _lib.csa_indexer_topk(inputs["q_I"], inputs["w"], plan.k_I_cmp, L.Tq, plan.H_I, plan.d_I, L.cu_seqlens_q,
-                                  L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r,
-                                  L.max_seqlen_kv, plan.topk, plan.topk_idx, None)
-
-    def mla():
-        cmp_idx = plan.topk_idx
-        _lib.csa_sparse_mla_fwd(inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx,
-                                plan.topk if cmp_idx is not None else 0, L.Tq, L.Tkv, plan.H, plan.d, L.cu_seqlens_q,
-                                L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r, plan.wl, plan.wr,
-                                inputs["sinks"], plan.scale, plan.out, None)
-
-    for _ in range(args.warmup):
-        front(); indexer(); mla()
-    torch.cuda.synchronize()
-
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    ev = [(E(), E(), E(), E()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for e0, e1, e2, e3 in ev:
-        e0.record(); front(); e1.record(); indexer(); e2.record(); mla(); e3.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    t_front = np.array([a.elapsed_time(b) for a, b, _, _ in ev])
-    t_idx = np.array([b.elapsed_time(c) for _, b, c, _ in ev])
-    t_mla = np.array([c.elapsed_time(d) for _, _, c, d in ev])
-    t_step = np.array([a.elapsed_time(d) for a, _, _, d in ev])
+    t = time_forward(plan, inputs, args.steps, args.warmup)
+    t_front, t_idx, t_mla, t_step, wall = t["front"], t["indexer"], t["mla"], t["step"], t["wall"]
     ms_step = float(t_step.mean())
     tokens_s = pack.Tq / (ms_step / 1e3)
 
@@ -428,6 +488,13 @@ def main():
         result["indexer_kl"] = kl_bench(plan, pack, inputs, ncmp, args.bwd_steps, 2)
     if not args.no_learned and plan.r == 4 and plan.Tc_cap > 0:
         result["learned_compressor"] = learned_bench(plan, pack, args.bwd_steps, 2)
+    if not args.no_workloads:
+        del inputs, plan
+        torch.cuda.empty_cache()
+        result["workloads"] = {}
+        for name in ("single4k", "hca32k", "cp32k"):
+            if name != args.workload:
+                result["workloads"][name] = workload_bench(name, args.seed, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pack, args.cpu_budget)
     print(json.dumps(result), flush=True)

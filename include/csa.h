@@ -162,22 +162,37 @@ int csa_compress_learned(const void* x, int32_t Tkv, int32_t D, int32_t dtype, c
  * ascending order (stream-absolute compressed-row ids, as on [MI] 评论区精华
  * item 1), then -1.  topk_score (optional, may be NULL) holds each kept row's
  * score aligned with topk_idx, -inf in empty slots.
- *   q_I [Tq, H_I, d_I], w [Tq, H_I] (call dtype), k_I_cmp [Tc_cap, d_I] (call dtype,
+ *   q_I [Tq, H_I, d_I], w [Tq, H_I] (call dtype), k_I_cmp [Tc, d_I] (call dtype,
  *   from csa_compress), topk_idx [Tq, topk] int32, topk_score [Tq, topk] float32.
- * `max_seqlen_kv` must bound every segment length; it sizes on-chip score
+ * Tc is the number of rows k_I_cmp holds: candidates at or past
+ * min(Tc, cu_seqlens_cmp[B]) are never read (they do not exist).
+ * cmp_residual (optional, [B] int32 device, may be NULL): the per-segment tail
+ * count len_b mod r that the operator schema carries as cmp_residual_k ([HP] 1.,
+ * item 9; 背景 1: it fixes the valid compressed range).  Here cu_seqlens_kv already
+ * fixes that range, so the value must equal len_b mod r (what csa_build_indices
+ * writes); a query whose segment disagrees gets an all -1 row (and NaN scores), so
+ * a stale residual shows in the output instead of passing silently.
+ * The scores live in on-chip memory: the call needs no workspace.
+ * `max_seqlen_kv` must bound every segment length; it sizes that on-chip score
  * storage (floor(max_seqlen_kv / r) candidates per query).  Segments longer than
  * it give unspecified (but in-bounds) results.
- * Errors: EINVAL for NULL required pointers, B < 1, Tq < 0, H_I < 1, d_I < 1,
+ * Errors: EINVAL for NULL required pointers, B < 1, Tq < 0, Tc < 0, H_I < 1, d_I < 1,
  * topk < 1, cmp_ratio < 1, max_seqlen_kv < 0; EUNSUPPORTED for
  * floor(max_seqlen_kv / r) > 32768 candidates, topk > 2048, or a shape other
  * than (H_I, d_I) = (64, 128) bf16 or H_I * d_I <= 8192 with d_I % 8 == 0.
  */
 int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
-                     int32_t Tq, int32_t H_I, int32_t d_I, int32_t dtype,
+                     int32_t Tq, int32_t Tc, int32_t H_I, int32_t d_I, int32_t dtype,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                     const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start,
-                     int32_t cmp_ratio, int32_t max_seqlen_kv, int32_t topk,
+                     const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, int32_t B,
+                     int32_t global_start, int32_t cmp_ratio, int32_t max_seqlen_kv, int32_t topk,
                      int32_t* topk_idx, float* topk_score, csa_stream_t stream);
+
+/* How the rows of a cmp_idx argument were formed (csa_sparse_mla_fwd). */
+enum {
+  CSA_IDX_ANY = 0,  /* any entries, any order: entries outside [0, Tc) are skipped */
+  CSA_IDX_TOPK = 1  /* csa_indexer_topk's output for this layout and topk (see below) */
+};
 
 /*
  * csa_sparse_mla_fwd - sparse MLA forward over one shared latent KV
@@ -188,7 +203,7 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
  *   window rows   ori_kv[lo .. hi], lo = max(s_b, t - ori_win_left),
  *                 hi = min(e_b - 1, t + ori_win_right)   (band parameters, not an
  *                 index list: [HP] 对照实验 shows ori_sparse_indices is ignored)
- *   compressed    cmp_kv[c] for every c >= 0 in cmp_idx[i, 0:topk]  (sparse), or
+ *   compressed    cmp_kv[c] for every valid c in cmp_idx[i, 0:topk]  (sparse), or
  *                 every causally complete row of the segment when cmp_idx is NULL
  *                 (compressor-only layers, [MS] 主要改动 LayerCompressMode), or
  *                 none when cmp_kv is NULL (no compression).
@@ -196,22 +211,40 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
  * sink: logits z = softmax_scale * <q[i,h], key>, the sink logit sinks[h] (not
  * scaled) adds exp(sinks[h]) to the denominator with a zero value.  Online
  * softmax in float32; MFMA products of bf16 inputs with float32 accumulation.
- *   q [Tq, H, d], ori_kv [Tkv, d], cmp_kv [Tc_cap, d] (call dtype),
+ *   q [Tq, H, d], ori_kv [Tkv, d], cmp_kv [Tc, d] (call dtype),
  *   cmp_idx [Tq, topk] int32, sinks [H] float32 (NULL = no sink),
  *   out [Tq, H, d] (call dtype), lse [Tq, H] float32 (NULL = not written):
  *   natural log of the full denominator in the scaled-logit domain.
+ * Tc is the number of rows cmp_kv holds; rows at or past min(Tc, cu_seqlens_cmp[B])
+ * are never read.
+ * cmp_idx_kind says how the cmp_idx rows were formed:
+ *   CSA_IDX_ANY   valid entries are those in [0, min(Tc, cu_seqlens_cmp[B])), in any
+ *                 order; the others are skipped.
+ *   CSA_IDX_TOPK  the rows are csa_indexer_topk's output for the same layout, Tc
+ *                 and topk.  The top-k of at most topk candidates is all of them
+ *                 ([HP] 1.), so for a query with at most topk visible compressed
+ *                 rows the row lists exactly those rows and the call does not read
+ *                 it; otherwise the row holds exactly topk rows, used as given
+ *                 (each entry clamped into the buffer).  Rows that are not such
+ *                 output give unspecified results; every read stays in bounds.
+ * cmp_residual (optional, [B] int32 device, may be NULL): the per-segment tail
+ * count len_b mod r of the operator schema (cmp_residual_kv, [HP] 2.; required
+ * there when cmp_ratio != 1).  cu_seqlens_kv fixes the same quantity here, so the
+ * value must equal len_b mod r; a query whose segment disagrees gets NaN in out
+ * and lse, so a stale residual shows in the output instead of passing silently
+ * (the page's control experiment finds the operator's output depends on it).
  * Errors: EINVAL for NULL q/ori_kv/out/cu_seqlens*, cmp_idx without cmp_kv,
- * topk < 1 with cmp_idx, B < 1, Tq < 0, a window side < 0 (or Tkv plus both sides
- * >= 2^31), cmp_ratio < 1,
+ * topk < 1 with cmp_idx, an unknown cmp_idx_kind, B < 1, Tq < 0, Tc < 0, a window
+ * side < 0 (or Tkv plus both sides >= 2^31), cmp_ratio < 1,
  * global_start + Tq > Tkv, softmax_scale not positive and finite; EUNSUPPORTED for
  * shapes other than (H, d) = (64, 512)
  * bf16 or H * d <= 8192 with d % 8 == 0, or topk > 2048.
  */
 int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
-                       int32_t topk, int32_t Tq, int32_t Tkv, int32_t H, int32_t d, int32_t dtype,
-                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                       const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start,
-                       int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
+                       int32_t topk, int32_t cmp_idx_kind, int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H,
+                       int32_t d, int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                       const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, int32_t B,
+                       int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
                        const float* sinks, float softmax_scale, void* out, float* lse,
                        csa_stream_t stream);
 
@@ -307,12 +340,17 @@ int csa_indexer_kl_grad(const void* q_I, const void* w, const void* k_I_cmp, con
  * csa_validate_layout - synchronous debug check of a THD layout held in device
  * memory: cu_seqlens_kv starts at 0, is non-decreasing and ends at Tkv;
  * cu_seqlens_q equals clamp(cu_seqlens_kv - global_start, 0, Tq); and the longest
- * segment is at most max_seqlen_kv (pass -1 to skip that check).  Copies the two
- * arrays to the host (blocks on `stream`).  Returns CSA_OK or CSA_EINVAL with a
- * message naming the first violated condition.
+ * segment is at most max_seqlen_kv (pass -1 to skip that check).  With cmp_ratio
+ * >= 1 it also checks the compressed layout a caller holds: cu_seqlens_cmp (if not
+ * NULL) must be the prefix sums of floor(len_b / cmp_ratio) and cmp_residual (if
+ * not NULL) must equal len_b mod cmp_ratio ([HP] 背景 1: the residual is the original
+ * length mod cmp_ratio); pass cmp_ratio = 0 to skip both.  Copies the arrays to
+ * the host (blocks on `stream`).  Returns CSA_OK or CSA_EINVAL with a message naming
+ * the first violated condition.
  */
 int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B,
                         int32_t Tq, int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv,
+                        int32_t cmp_ratio, const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual,
                         csa_stream_t stream);
 
 #ifdef __cplusplus

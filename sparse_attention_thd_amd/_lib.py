@@ -17,6 +17,7 @@ LIB_PATH = os.environ.get("CSA_LIBRARY") or os.path.join(os.path.dirname(os.path
 
 CSA_OK, CSA_EINVAL, CSA_EUNSUPPORTED, CSA_EHIP = 0, 1, 2, 4
 CSA_F32, CSA_BF16 = 0, 1
+CSA_IDX_ANY, CSA_IDX_TOPK = 0, 1
 
 _P = C.c_void_p
 _I = C.c_int32
@@ -28,8 +29,8 @@ SIGNATURES = {
     "csa_build_indices": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P],
     "csa_compress": [_P, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P],
     "csa_compress_learned": [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _P],
-    "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
-    "csa_sparse_mla_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P,
+    "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
+    "csa_sparse_mla_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P,
                            C.c_float, _P, _P, _P],
     "csa_sparse_mla_bwd_workspace_bytes": [_I, _I, _I, _P, _P, _I, _I, _I],
     "csa_sparse_mla_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
@@ -37,7 +38,7 @@ SIGNATURES = {
     "csa_indexer_kl_grad_workspace_bytes": [_I, _I, _I, _I],
     "csa_indexer_kl_grad": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                             _P, _P, _P, _P, _P, C.c_int64, _P],
-    "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _P],
+    "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
 }
 RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64,
             "csa_indexer_kl_grad_workspace_bytes": C.c_int64}
@@ -146,30 +147,33 @@ def csa_compress_learned(x, Tkv, D, wkv, wgate, ape, hd, overlap, cu_seqlens_kv,
                                     _ptr(x_cmp, "x_cmp", x.dtype, need=Tc_cap * hd), Tc_cap, _stream(stream)))
 
 
-def csa_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
-                     cmp_ratio, max_seqlen_kv, topk, topk_idx, topk_score=None, stream=None):
+def csa_indexer_topk(q_I, w, k_I_cmp, Tq, Tc, H_I, d_I, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, cmp_residual,
+                     B, global_start, cmp_ratio, max_seqlen_kv, topk, topk_idx, topk_score=None, stream=None):
     i32 = torch.int32
     dt = q_I.dtype
     _check(LIB.csa_indexer_topk(
-        _ptr(q_I, "q_I", need=Tq * H_I * d_I), _ptr(w, "w", dt, need=Tq * H_I), _ptr(k_I_cmp, "k_I_cmp", dt), Tq,
-        H_I, d_I, _dtype_code(q_I), _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1),
-        _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1), _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1),
+        _ptr(q_I, "q_I", need=Tq * H_I * d_I), _ptr(w, "w", dt, need=Tq * H_I),
+        _ptr(k_I_cmp, "k_I_cmp", dt, Tc == 0, Tc * d_I), Tq, Tc, H_I, d_I, _dtype_code(q_I),
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1), _ptr(cmp_residual, "cmp_residual", i32, True, B),
         B, global_start, cmp_ratio, max_seqlen_kv, topk, _ptr(topk_idx, "topk_idx", i32, need=Tq * topk),
         _ptr(topk_score, "topk_score", torch.float32, True, Tq * topk), _stream(stream)))
 
 
-def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, H, d, cu_seqlens_q, cu_seqlens_kv,
-                       cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, sinks,
+def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, cmp_idx_kind, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv,
+                       cu_seqlens_cmp, cmp_residual, B, global_start, cmp_ratio, ori_win_left, ori_win_right, sinks,
                        softmax_scale, out, lse=None, stream=None):
     i32 = torch.int32
     dt = q.dtype
     _check(LIB.csa_sparse_mla_fwd(
-        _ptr(q, "q", need=Tq * H * d), _ptr(ori_kv, "ori_kv", dt, need=Tkv * d), _ptr(cmp_kv, "cmp_kv", dt, True),
-        _ptr(cmp_idx, "cmp_idx", i32, True, Tq * topk), topk, Tq, Tkv, H, d, _dtype_code(q),
+        _ptr(q, "q", need=Tq * H * d), _ptr(ori_kv, "ori_kv", dt, need=Tkv * d),
+        _ptr(cmp_kv, "cmp_kv", dt, True, Tc * d), _ptr(cmp_idx, "cmp_idx", i32, True, Tq * topk), topk, cmp_idx_kind,
+        Tq, Tkv, Tc, H, d, _dtype_code(q),
         _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
-        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True, B + 1), B, global_start, cmp_ratio, ori_win_left,
-        ori_win_right, _ptr(sinks, "sinks", torch.float32, True, H), float(softmax_scale),
-        _ptr(out, "out", dt, need=Tq * H * d), _ptr(lse, "lse", torch.float32, True, Tq * H), _stream(stream)))
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True, B + 1), _ptr(cmp_residual, "cmp_residual", i32, True, B),
+        B, global_start, cmp_ratio, ori_win_left, ori_win_right, _ptr(sinks, "sinks", torch.float32, True, H),
+        float(softmax_scale), _ptr(out, "out", dt, need=Tq * H * d), _ptr(lse, "lse", torch.float32, True, Tq * H),
+        _stream(stream)))
 
 
 def csa_sparse_mla_bwd_workspace_bytes(Tq, ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv,
@@ -227,8 +231,11 @@ def csa_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, H_I, d_
         _ptr(loss, "loss", f32, True, Tq), _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
 
 
-def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, stream=None):
+def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, cmp_ratio=0,
+                        cu_seqlens_cmp=None, cmp_residual=None, stream=None):
     i32 = torch.int32
     _check(LIB.csa_validate_layout(_ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1),
                                    _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1), B, Tq, Tkv, global_start,
-                                   max_seqlen_kv, _stream(stream)))
+                                   max_seqlen_kv, cmp_ratio,
+                                   _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True, B + 1),
+                                   _ptr(cmp_residual, "cmp_residual", i32, True, B), _stream(stream)))

@@ -146,14 +146,14 @@ class CsaPlan:
             else:
                 _lib.csa_compress(k_I, L.Tkv, self.d_I, L.cu_seqlens_kv, self.cu_seqlens_cmp, L.B, self.r,
                                   self.k_I_cmp, self.Tc_cap, stream)
-            _lib.csa_indexer_topk(q_I, w, self.k_I_cmp, L.Tq, self.H_I, self.d_I, L.cu_seqlens_q, L.cu_seqlens_kv,
-                                  self.cu_seqlens_cmp, L.B, L.global_start, self.r, L.max_seqlen_kv, self.topk,
-                                  self.topk_idx, self.topk_score, stream)
+            _lib.csa_indexer_topk(q_I, w, self.k_I_cmp, L.Tq, self.Tc_cap, self.H_I, self.d_I, L.cu_seqlens_q,
+                                  L.cu_seqlens_kv, self.cu_seqlens_cmp, self.cmp_residual, L.B, L.global_start, self.r,
+                                  L.max_seqlen_kv, self.topk, self.topk_idx, self.topk_score, stream)
             cmp_idx = self.topk_idx
-        _lib.csa_sparse_mla_fwd(q, ori_kv, self.cmp_kv, cmp_idx, self.topk if cmp_idx is not None else 0, L.Tq,
-                                L.Tkv, self.H, self.d, L.cu_seqlens_q, L.cu_seqlens_kv, self.cu_seqlens_cmp, L.B,
-                                L.global_start, self.r, self.wl, self.wr, sinks, self.scale, self.out, self.lse,
-                                stream)
+        _lib.csa_sparse_mla_fwd(q, ori_kv, self.cmp_kv, cmp_idx, self.topk if cmp_idx is not None else 0,
+                                _lib.CSA_IDX_TOPK, L.Tq, L.Tkv, self.Tc_cap if self.cmp_kv is not None else 0, self.H,
+                                self.d, L.cu_seqlens_q, L.cu_seqlens_kv, self.cu_seqlens_cmp, self.cmp_residual, L.B,
+                                L.global_start, self.r, self.wl, self.wr, sinks, self.scale, self.out, self.lse, stream)
         return self.out
 
 

@@ -114,15 +114,16 @@ int csa_compress_learned(const void* x, int32_t Tkv, int32_t D, int32_t dtype, c
                     "csa_compress_learned");
 }
 
-int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_t Tq, int32_t H_I, int32_t d_I,
-                     int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
-                     const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
-                     int32_t max_seqlen_kv, int32_t topk, int32_t* topk_idx, float* topk_score,
+int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_t Tq, int32_t Tc, int32_t H_I,
+                     int32_t d_I, int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                     const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, int32_t B, int32_t global_start,
+                     int32_t cmp_ratio, int32_t max_seqlen_kv, int32_t topk, int32_t* topk_idx, float* topk_score,
                      csa_stream_t stream) {
-  if (!cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp || !k_I_cmp ||
+  if (!cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp || (Tc > 0 && !k_I_cmp) ||
       (Tq != 0 && (!q_I || !w || !topk_idx)))
     return fail(CSA_EINVAL, "csa_indexer_topk: NULL pointer");
-  if (B < 1 || Tq < 0 || H_I < 1 || d_I < 1 || topk < 1 || cmp_ratio < 1 || max_seqlen_kv < 0 || global_start < 0)
+  if (B < 1 || Tq < 0 || Tc < 0 || H_I < 1 || d_I < 1 || topk < 1 || cmp_ratio < 1 || max_seqlen_kv < 0 ||
+      global_start < 0)
     return fail(CSA_EINVAL, "csa_indexer_topk: invalid size or parameter");
   if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_indexer_topk: unknown dtype %d", dtype);
   if (topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_indexer_topk: topk %d > %d", topk, kMaxTopk);
@@ -132,23 +133,26 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_
                 kMaxCandidates);
   if (!csa::indexer_shape_supported(H_I, d_I, dtype))
     return fail(CSA_EUNSUPPORTED, "csa_indexer_topk: no kernel for H_I=%d d_I=%d dtype=%d", H_I, d_I, dtype);
-  return hip_status(csa::launch_indexer_topk(q_I, w, k_I_cmp, Tq, H_I, d_I, dtype, cu_seqlens_q, cu_seqlens_kv,
-                                             cu_seqlens_cmp, B, global_start, cmp_ratio, cap, topk, topk_idx,
-                                             topk_score, static_cast<hipStream_t>(stream)),
+  return hip_status(csa::launch_indexer_topk(q_I, w, k_I_cmp, Tq, Tc, H_I, d_I, dtype, cu_seqlens_q, cu_seqlens_kv,
+                                             cu_seqlens_cmp, cmp_residual, B, global_start, cmp_ratio, cap, topk,
+                                             topk_idx, topk_score, static_cast<hipStream_t>(stream)),
                     "csa_indexer_topk");
 }
 
 int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
-                       int32_t Tq, int32_t Tkv, int32_t H, int32_t d, int32_t dtype, const int32_t* cu_seqlens_q,
-                       const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp, int32_t B,
-                       int32_t global_start, int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
-                       const float* sinks, float softmax_scale, void* out, float* lse, csa_stream_t stream) {
+                       int32_t cmp_idx_kind, int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d,
+                       int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                       const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, int32_t B, int32_t global_start,
+                       int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right, const float* sinks,
+                       float softmax_scale, void* out, float* lse, csa_stream_t stream) {
   if (!cu_seqlens_q || !cu_seqlens_kv || !ori_kv || (Tq != 0 && (!q || !out)))
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: NULL pointer");
   if (cmp_kv && !cu_seqlens_cmp) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: cmp_kv needs cu_seqlens_cmp");
   if (cmp_idx && !cmp_kv) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: cmp_idx given without cmp_kv");
   if (cmp_idx && topk < 1) return fail(CSA_EINVAL, "csa_sparse_mla_fwd: topk must be >= 1 with cmp_idx");
-  if (B < 1 || Tq < 0 || Tkv < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0)
+  if (cmp_idx_kind != CSA_IDX_ANY && cmp_idx_kind != CSA_IDX_TOPK)
+    return fail(CSA_EINVAL, "csa_sparse_mla_fwd: unknown cmp_idx_kind %d", cmp_idx_kind);
+  if (B < 1 || Tq < 0 || Tkv < 0 || Tc < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0)
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: invalid size or parameter");
   if (!window_fits(ori_win_left, ori_win_right, Tkv))
     return fail(CSA_EINVAL, "csa_sparse_mla_fwd: window sides must be >= 0 with Tkv + sides < 2^31");
@@ -161,10 +165,10 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
   if (cmp_idx && topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_fwd: topk %d > %d", topk, kMaxTopk);
   if (!csa::mla_shape_supported(H, d, dtype))
     return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_fwd: no kernel for H=%d d=%d dtype=%d", H, d, dtype);
-  return hip_status(csa::launch_sparse_mla(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, H, d, dtype, cu_seqlens_q,
-                                           cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left,
-                                           ori_win_right, sinks, softmax_scale, out, lse,
-                                           static_cast<hipStream_t>(stream)),
+  return hip_status(csa::launch_sparse_mla(q, ori_kv, cmp_kv, cmp_idx, topk, cmp_idx_kind == CSA_IDX_TOPK, Tq,
+                                           cmp_kv ? Tc : 0, H, d, dtype, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp,
+                                           cmp_residual, B, global_start, cmp_ratio, ori_win_left, ori_win_right,
+                                           sinks, softmax_scale, out, lse, static_cast<hipStream_t>(stream)),
                     "csa_sparse_mla_fwd");
 }
 
@@ -274,14 +278,20 @@ int csa_indexer_kl_grad(const void* q_I, const void* w, const void* k_I_cmp, con
 }
 
 int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B, int32_t Tq,
-                        int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv, csa_stream_t stream) {
-  if (!cu_seqlens_q || !cu_seqlens_kv || B < 1 || Tq < 0 || Tkv < 0 || global_start < 0)
+                        int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv, int32_t cmp_ratio,
+                        const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv || B < 1 || Tq < 0 || Tkv < 0 || global_start < 0 || cmp_ratio < 0)
     return fail(CSA_EINVAL, "csa_validate_layout: invalid argument");
-  std::vector<int32_t> cq(B + 1), ck(B + 1);
+  std::vector<int32_t> cq(B + 1), ck(B + 1), cc(B + 1), rs(B);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool want_cmp = cmp_ratio >= 1 && cu_seqlens_cmp, want_res = cmp_ratio >= 1 && cmp_residual;
   hipError_t e = hipMemcpyAsync(cq.data(), cu_seqlens_q, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
   if (e == hipSuccess)
     e = hipMemcpyAsync(ck.data(), cu_seqlens_kv, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && want_cmp)
+    e = hipMemcpyAsync(cc.data(), cu_seqlens_cmp, sizeof(int32_t) * (B + 1), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && want_res)
+    e = hipMemcpyAsync(rs.data(), cmp_residual, sizeof(int32_t) * B, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_status(e, "csa_validate_layout");
   if (ck[0] != 0) return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_kv[0] = %d, expected 0", ck[0]);
@@ -297,6 +307,20 @@ int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k
     want = want < 0 ? 0 : (want > Tq ? Tq : want);
     if (cq[b] != want)
       return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_q[%d] = %d, expected %lld", b, cq[b], want);
+  }
+  long long acc = 0;
+  for (int b = 0; b < B; ++b) {
+    const int len = ck[b + 1] - ck[b];
+    if (want_cmp) {
+      if (cc[b] != acc)
+        return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_cmp[%d] = %d, expected %lld", b, cc[b], acc);
+      acc += len / cmp_ratio;
+      if (b + 1 == B && cc[B] != acc)
+        return fail(CSA_EINVAL, "csa_validate_layout: cu_seqlens_cmp[%d] = %d, expected %lld", B, cc[B], acc);
+    }
+    if (want_res && rs[b] != len % cmp_ratio)
+      return fail(CSA_EINVAL, "csa_validate_layout: cmp_residual[%d] = %d, expected %d (segment length %d mod %d)",
+                  b, rs[b], len % cmp_ratio, len, cmp_ratio);
   }
   return CSA_OK;
 }

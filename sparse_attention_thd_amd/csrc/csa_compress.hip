@@ -23,12 +23,14 @@ struct Chunk<uint16_t> {  // bf16: 8 elements per 16 bytes
       acc[2 * k + 1] += static_cast<double>(__uint_as_float(w[k] & 0xffff0000u));
     }
   }
-  __device__ static uint4 finish(const double* acc, double inv_r) {
+  // The mean is the correctly rounded float64 quotient sum / r, then one rounding to
+  // the storage type (a product with 1 / r would round twice for r not a power of two).
+  __device__ static uint4 finish(const double* acc, double r) {
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t lo = f64_to_bf16_bits(acc[2 * k] * inv_r);
-      const uint32_t hi = f64_to_bf16_bits(acc[2 * k + 1] * inv_r);
+      const uint32_t lo = f64_to_bf16_bits(acc[2 * k] / r);
+      const uint32_t hi = f64_to_bf16_bits(acc[2 * k + 1] / r);
       w[k] = lo | (hi << 16);
     }
     return make_uint4(w[0], w[1], w[2], w[3]);
@@ -43,11 +45,11 @@ struct Chunk<float> {  // f32: 4 elements per 16 bytes
     acc[2] += static_cast<double>(__uint_as_float(v.z));
     acc[3] += static_cast<double>(__uint_as_float(v.w));
   }
-  __device__ static uint4 finish(const double* acc, double inv_r) {
-    return make_uint4(__float_as_uint(static_cast<float>(acc[0] * inv_r)),
-                      __float_as_uint(static_cast<float>(acc[1] * inv_r)),
-                      __float_as_uint(static_cast<float>(acc[2] * inv_r)),
-                      __float_as_uint(static_cast<float>(acc[3] * inv_r)));
+  __device__ static uint4 finish(const double* acc, double r) {
+    return make_uint4(__float_as_uint(static_cast<float>(acc[0] / r)),
+                      __float_as_uint(static_cast<float>(acc[1] / r)),
+                      __float_as_uint(static_cast<float>(acc[2] / r)),
+                      __float_as_uint(static_cast<float>(acc[3] / r)));
   }
 };
 
@@ -62,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(const T* __restrict_
   const int b = segment_of(cu_cmp, B, c);
   const long long first = static_cast<long long>(cu_kv[b]) + static_cast<long long>(c - cu_cmp[b]) * r;
   const int nchunk = d / Chunk<T>::N;
-  const double inv_r = 1.0 / static_cast<double>(r);
+  const double rd = static_cast<double>(r);
   for (int ch = lane; ch < nchunk; ch += 64) {
     double acc[Chunk<T>::N];
 #pragma unroll
@@ -81,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void compress_kernel(const T* __restrict_
       Chunk<T>::add(acc, v3);
     }
     for (; m < r; ++m) Chunk<T>::add(acc, src[m * stride]);
-    reinterpret_cast<uint4*>(x_cmp + static_cast<long long>(c) * d)[ch] = Chunk<T>::finish(acc, inv_r);
+    reinterpret_cast<uint4*>(x_cmp + static_cast<long long>(c) * d)[ch] = Chunk<T>::finish(acc, rd);
   }
 }
 

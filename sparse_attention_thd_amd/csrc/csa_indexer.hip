@@ -240,14 +240,43 @@ __device__ void score_mfma_64x128_pair(const uint16_t* __restrict__ q_I, const u
   }
 }
 
+// Candidate range of local query i: rows [lo, lo + nv) of its segment b that are
+// causally complete, exist in the k_cmp buffer (Tc rows) and fit the score storage.
+// With a caller-held residual that disagrees with the segment length, nv = -1 (the
+// query's row is then written as all -1).
+__device__ __forceinline__ void candidate_range(int i, const int32_t* __restrict__ cu_q,
+                                                const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
+                                                const int32_t* __restrict__ residual, int B, int global_start, int r,
+                                                int cap, int Tc, int& lo, int& nv) {
+  const int b = segment_of(cu_q, B, i);
+  const int s = cu_kv[b];
+  const int p = global_start + i - s;
+  lo = cu_cmp[b];
+  int v = (p + 1) / r;
+  v = min(v, cu_cmp[b + 1] - lo);
+  v = min(v, Tc - lo);
+  nv = max(0, min(v, cap));
+  if (residual != nullptr && residual[b] != (cu_kv[b + 1] - s) % r) nv = -1;
+}
+
+// The row of a query whose segment's residual disagrees: no selection, NaN scores.
+__device__ __forceinline__ void write_poisoned_row(int32_t* __restrict__ out_idx, float* __restrict__ out_sc,
+                                                   int topk) {
+  for (int k = threadIdx.x; k < topk; k += kThreads) {
+    out_idx[k] = -1;
+    if (out_sc) out_sc[k] = __builtin_nanf("");
+  }
+}
+
 // (H_I, d_I) = (64, 128) bf16, two queries per workgroup: queries 2 x and 2 x + 1.
 // A query with no more candidates than top-k only writes its ascending list.  Two
 // selecting queries of one segment are scored in one pass (above); otherwise each is
 // scored alone.  The selections then run one after the other.
 __global__ __launch_bounds__(kThreads) void indexer_topk_pair_kernel(
     const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B,
-    int global_start, int r, int cap, int topk, int Tq, int32_t* __restrict__ idx, float* __restrict__ score) {
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
+    const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk, int Tq,
+    int32_t* __restrict__ idx, float* __restrict__ score) {
   extern __shared__ uint32_t dyn[];  // two key arrays of cap entries
   __shared__ SelectShared sh;
   const int i0 = 2 * static_cast<int>(blockIdx.x);
@@ -259,12 +288,13 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_pair_kernel(
   for (int e = 0; e < 2; ++e) {
     if (e >= nq) break;
     const int i = i0 + e;
-    const int b = segment_of(cu_q, B, i);
-    const int p = global_start + i - cu_kv[b];
-    lo[e] = cu_cmp[b];
-    int v = (p + 1) / r;
-    v = min(v, cu_cmp[b + 1] - lo[e]);
-    nv[e] = max(0, min(v, cap));
+    candidate_range(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap, Tc, lo[e], nv[e]);
+    if (nv[e] < 0) {
+      write_poisoned_row(idx + static_cast<long long>(i) * topk, score ? score + static_cast<long long>(i) * topk : nullptr,
+                         topk);
+      nv[e] = 0;
+      continue;
+    }
     heavy[e] = !(nv[e] <= topk && score == nullptr);
     if (!heavy[e]) {
       int32_t* out_idx = idx + static_cast<long long>(i) * topk;
@@ -304,22 +334,22 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(const T* __restr
                                                                 const T* __restrict__ k_cmp, int H_I, int d_I,
                                                                 const int32_t* __restrict__ cu_q,
                                                                 const int32_t* __restrict__ cu_kv,
-                                                                const int32_t* __restrict__ cu_cmp, int B,
-                                                                int global_start, int r, int cap, int topk,
+                                                                const int32_t* __restrict__ cu_cmp,
+                                                                const int32_t* __restrict__ residual, int B,
+                                                                int global_start, int r, int cap, int Tc, int topk,
                                                                 int32_t* __restrict__ idx, float* __restrict__ score) {
   extern __shared__ uint32_t dyn[];
   __shared__ SelectShared sh;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
-  const int b = segment_of(cu_q, B, i);
-  const int t = global_start + i;
-  const int p = t - cu_kv[b];
-  const int lo = cu_cmp[b];
-  int nv = (p + 1) / r;
-  nv = min(nv, cu_cmp[b + 1] - lo);
-  nv = max(0, min(nv, cap));
+  int lo, nv;
+  candidate_range(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap, Tc, lo, nv);
   int32_t* out_idx = idx + static_cast<long long>(i) * topk;
   float* out_sc = score ? score + static_cast<long long>(i) * topk : nullptr;
+  if (nv < 0) {
+    write_poisoned_row(out_idx, out_sc, topk);
+    return;
+  }
   if (nv <= topk && out_sc == nullptr) {
     for (int k = tid; k < topk; k += kThreads) out_idx[k] = (k < nv) ? lo + k : -1;
     return;
@@ -348,10 +378,10 @@ bool indexer_shape_supported(int H_I, int d_I, int dtype) {
   return H_I * d_I <= 8192 && d_I % 8 == 0;
 }
 
-hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp, int Tq, int H_I, int d_I,
+hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp, int Tq, int Tc, int H_I, int d_I,
                                int dtype, const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_cmp,
-                               int B, int global_start, int r, int cap, int topk, int32_t* idx, float* score,
-                               hipStream_t s) {
+                               const int32_t* residual, int B, int global_start, int r, int cap, int topk,
+                               int32_t* idx, float* score, hipStream_t s) {
   if (Tq <= 0) return hipSuccess;
   const bool mfma = (dtype == 1 && H_I == 64 && d_I == 128);
   size_t lds = static_cast<size_t>(cap) * 4;
@@ -368,30 +398,30 @@ hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp
     if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
       return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
-                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r,
-                       cap, topk, idx, score);
+                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
+                       cap, Tc, topk, idx, score);
   } else if (mfma) {
     auto k = indexer_topk_pair_kernel;
     const size_t lds2 = 2 * static_cast<size_t>(cap) * 4;
     if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds2); e != hipSuccess)
       return e;
     hipLaunchKernelGGL(k, dim3((Tq + 1) / 2), block, lds2, s, static_cast<const uint16_t*>(q_I),
-                       static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(k_cmp), cu_q, cu_kv, cu_cmp, B,
-                       global_start, r, cap, topk, Tq, idx, score);
+                       static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(k_cmp), cu_q, cu_kv, cu_cmp, residual, B,
+                       global_start, r, cap, Tc, topk, Tq, idx, score);
   } else if (dtype == 1) {
     auto k = indexer_topk_kernel<0, uint16_t>;
     if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
       return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
-                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r,
-                       cap, topk, idx, score);
+                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
+                       cap, Tc, topk, idx, score);
   } else {
     auto k = indexer_topk_kernel<0, float>;
     if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
       return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const float*>(q_I), static_cast<const float*>(w),
-                       static_cast<const float*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, B, global_start, r, cap,
-                       topk, idx, score);
+                       static_cast<const float*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap,
+                       Tc, topk, idx, score);
   }
   return hipGetLastError();
 }

@@ -36,10 +36,13 @@ __device__ __forceinline__ int segment_of_wave(const int32_t* __restrict__ cu, i
   return __builtin_amdgcn_readfirstlane(count - 1);
 }
 
-// Resolve the query's window and compressed key ranges.
+// Resolve the query's window and compressed key ranges.  Compressed rows are bounded by
+// the segment and by the Tc rows the cmp_kv buffer holds.  `bad` is set when a
+// caller-held residual disagrees with the segment length.
 __device__ QueryKeys query_ranges(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
-                                  const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
-                                  bool has_cmp, bool attend_all) {
+                                  const int32_t* __restrict__ cu_cmp, const int32_t* __restrict__ residual, int B,
+                                  int global_start, int r, int wl, int wr, int Tc, bool has_cmp, bool attend_all,
+                                  bool& bad) {
   QueryKeys k;
   const int b = segment_of_wave(cu_q, B, i);
   const int t = global_start + i;
@@ -51,17 +54,20 @@ __device__ QueryKeys query_ranges(int i, const int32_t* __restrict__ cu_q, const
   k.cmp_base = (cu_cmp != nullptr) ? cu_cmp[b] : 0;
   if (has_cmp && attend_all) {
     const int nv = (t - s + 1) / r;
-    k.ncmp = max(0, min(nv, cu_cmp[b + 1] - k.cmp_base));
+    k.ncmp = max(0, min(min(nv, cu_cmp[b + 1] - k.cmp_base), Tc - k.cmp_base));
   }
+  bad = residual != nullptr && residual[b] != (e - s) % r;
   return k;
 }
 
 // Generic-path helper: ranges plus compaction, loading the cmp_idx row itself.
 __device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
-                                const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr,
-                                bool has_cmp, const int32_t* __restrict__ cmp_idx, int topk, int32_t* crow,
-                                uint32_t* wsum) {
-  QueryKeys k = query_ranges(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, has_cmp, cmp_idx == nullptr);
+                                const int32_t* __restrict__ cu_cmp, const int32_t* __restrict__ residual, int B,
+                                int global_start, int r, int wl, int wr, int Tc, bool has_cmp,
+                                const int32_t* __restrict__ cmp_idx, int topk, int32_t* crow, uint32_t* wsum,
+                                bool& bad) {
+  QueryKeys k = query_ranges(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, wl, wr, Tc, has_cmp,
+                             cmp_idx == nullptr, bad);
   if (!has_cmp || cmp_idx == nullptr) return k;
   const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
   int vals[kMaxTopk / kThreads];
@@ -70,7 +76,7 @@ __device__ QueryKeys query_keys(int i, const int32_t* __restrict__ cu_q, const i
     const int j = ch * kThreads + static_cast<int>(threadIdx.x);
     vals[ch] = (j < topk) ? row[j] : -1;
   }
-  k.ncmp = compact_rows(vals, topk, cu_cmp[B], crow, wsum);
+  k.ncmp = compact_rows(vals, topk, min(cu_cmp[B], Tc), crow, wsum);
   return k;
 }
 
@@ -82,9 +88,10 @@ constexpr int kVD = 4;                       // V^T-fragment prefetch distance (
 template <int NC>  // cmp_idx row chunks of kThreads entries: ceil(topk / 256)
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mla_fwd_h64_d512_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ ori_kv, const uint16_t* __restrict__ cmp_kv,
-    const int32_t* __restrict__ cmp_idx, int topk, int Tq, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
-    int wr, const float* __restrict__ sinks, float scale_log2, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ cmp_idx, int topk, int topk_rows, int Tq, int Tc, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, const int32_t* __restrict__ residual, int B,
+    int global_start, int r, int wl, int wr, const float* __restrict__ sinks, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) unsigned char kt[2 * kTileBytes];
   __shared__ __attribute__((aligned(16))) unsigned char pfr[kWaves * 64 * 16];  // P^T fragments of the tile
   __shared__ float alpha_h[64];  // per-head rescale factor of the tile (1 when not rescaled)
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int head = 16 * wave + n;
-  const bool sparse = cmp_kv != nullptr && cmp_idx != nullptr;
+  const bool has_idx = cmp_kv != nullptr && cmp_idx != nullptr;
 
   // Prologue loads are issued cheapest-first and all stay in flight together; each
   // later use waits only for the loads it needs (the counter retires them in order).
@@ -112,11 +119,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int cu0 = (lane < B) ? cu_q[lane] : 0x7fffffff;  // first 64 segment starts
   const int kv0 = (small_b && lane <= B) ? cu_kv[lane] : 0;
   const int cm0 = (small_b && lane <= B && cu_cmp != nullptr) ? cu_cmp[lane] : 0;
+  // An arbitrary index row is needed whatever the query's visible count: fetch it now.
+  const int32_t* idx_row = has_idx ? cmp_idx + static_cast<long long>(i) * topk : nullptr;
   int vals[NC];
-  if (sparse) {
-    const int32_t* row = cmp_idx + static_cast<long long>(i) * topk;
+  if (has_idx && !topk_rows) {
 #pragma unroll
-    for (int ch = 0; ch < NC; ++ch) vals[ch] = row[min(ch * kThreads + tid, topk - 1)];
+    for (int ch = 0; ch < NC; ++ch) vals[ch] = idx_row[min(ch * kThreads + tid, topk - 1)];
   }
   // The query's 64 q rows (64 KiB, contiguous) are staged through the idle tile buffers
   // as whole 1 KiB rows, one global_load_lds_dwordx4 per row (wave w: heads 16w ..
@@ -136,18 +144,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   QueryKeys qk;
   int cmp_end = 0, cmp_total = 0;  // cu_cmp[b + 1], cu_cmp[B]
   const int t_abs = global_start + i;
-  int seg_s;
+  int seg_s, seg_e;
   {
-    int e;
     if (small_b) {
       seg_s = __builtin_amdgcn_readlane(kv0, b);
-      e = __builtin_amdgcn_readlane(kv0, b + 1);
+      seg_e = __builtin_amdgcn_readlane(kv0, b + 1);
       qk.cmp_base = __builtin_amdgcn_readlane(cm0, b);
       cmp_end = __builtin_amdgcn_readlane(cm0, b + 1);
       cmp_total = __builtin_amdgcn_readlane(cm0, B);
     } else {
       seg_s = cu_kv[b];
-      e = cu_kv[b + 1];
+      seg_e = cu_kv[b + 1];
       if (cu_cmp != nullptr) {
         qk.cmp_base = cu_cmp[b];
         cmp_end = cu_cmp[b + 1];
@@ -157,23 +164,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     qk.lo = max(seg_s, t_abs - wl);
-    qk.nwin = min(e - 1, t_abs + wr) - qk.lo + 1;
+    qk.nwin = min(seg_e - 1, t_abs + wr) - qk.lo + 1;
     qk.ncmp = 0;
-    if (cmp_kv != nullptr && cmp_idx == nullptr) qk.ncmp = max(0, min((t_abs - seg_s + 1) / r, cmp_end - qk.cmp_base));
   }
-  // A tile that lies inside the window holds stream rows lo + 32 t + r, so every row
-  // address is wave-uniform: formed in scalar registers, no lane lookup.
-  auto issue_window_tile = [&](int t, int bf) {
-    const uint16_t* src = ori_kv + static_cast<long long>(qk.lo + t * kNT + wave) * 512;
+  // Compressed rows that exist: the segment's, inside the Tc rows of the buffer.
+  const int nvis = (cmp_kv != nullptr)
+                       ? max(0, min(min((t_abs - seg_s + 1) / r, cmp_end - qk.cmp_base), Tc - qk.cmp_base))
+                       : 0;
+  // Contiguous compressed rows [cmp_base, cmp_base + nvis): attend-all layers, and top-k
+  // rows of a query with at most topk visible rows (its top-k is all of them); none
+  // without compression.
+  const bool direct = cmp_kv == nullptr || cmp_idx == nullptr || (topk_rows && nvis <= topk);
+  if (direct) qk.ncmp = nvis;
+  // A caller-held residual that disagrees with the segment length poisons the output.
+  const bool bad = residual != nullptr && residual[b] != (seg_e - seg_s) % r;
+  // Every address of a direct query's tiles is wave-uniform (rows lo + k of the window,
+  // then cmp_base + k): formed in scalar registers, no lane lookup.
+  auto issue_direct_tile = [&](int t, int bf, int nkeys_) {
 #pragma unroll
-    for (int pass = 0; pass < kNT / kWaves; ++pass)
-      row_to_lds(src + pass * kWaves * 512, lane16,
-                 kt_base + static_cast<uint32_t>(bf * kTileBytes + (pass * kWaves + wave) * kRowStride));
+    for (int pass = 0; pass < kNT / kWaves; ++pass) {
+      int kidx = t * kNT + pass * kWaves + wave;
+      kidx = (kidx < nkeys_) ? kidx : 0;
+      const uint16_t* src = (kidx < qk.nwin) ? ori_kv + static_cast<long long>(qk.lo + kidx) * 512
+                                             : cmp_kv + static_cast<long long>(qk.cmp_base + kidx - qk.nwin) * 512;
+      row_to_lds(src, lane16, kt_base + static_cast<uint32_t>(bf * kTileBytes + (pass * kWaves + wave) * kRowStride));
+    }
   };
-  if (sparse) {
+  if (has_idx && !direct) {
+    if (topk_rows) {
+      // a selecting query: exactly topk rows, ascending, used as given (clamped into the buffer)
+      const int hi_row = max(0, min(cmp_total, Tc) - 1);
 #pragma unroll
-    for (int ch = 0; ch < NC; ++ch) vals[ch] = (ch * kThreads + tid < topk) ? vals[ch] : -1;
-    qk.ncmp = compact_rows(vals, topk, cmp_total, crow, wsum);
+      for (int ch = 0; ch < NC; ++ch) {
+        const int j = ch * kThreads + tid;
+        if (j < topk) crow[j] = min(max(idx_row[j], 0), hi_row);
+      }
+      qk.ncmp = topk;
+    } else {
+#pragma unroll
+      for (int ch = 0; ch < NC; ++ch) vals[ch] = (ch * kThreads + tid < topk) ? vals[ch] : -1;
+      qk.ncmp = compact_rows(vals, topk, min(cmp_total, Tc), crow, wsum);
+    }
   }
   const int nkeys = qk.nwin + qk.ncmp;
   const int ntiles = (nkeys + kNT - 1) / kNT;
@@ -185,8 +216,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // row.  Rows past the key list re-read a valid row; their
   // probabilities are exactly zero.
   auto issue = [&](int t, int bf) {
-    if ((t + 1) * kNT <= qk.nwin) {
-      issue_window_tile(t, bf);
+    if (direct || (t + 1) * kNT <= qk.nwin) {
+      issue_direct_tile(t, bf, nkeys);
       return;
     }
     const int p = lane & 7;
@@ -196,8 +227,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     if (kidx < qk.nwin) {
       src = ori_kv + static_cast<long long>(qk.lo + kidx) * 512;
     } else {
-      const int c = (cmp_idx != nullptr) ? crow[kidx - qk.nwin] : qk.cmp_base + (kidx - qk.nwin);
-      src = cmp_kv + static_cast<long long>(c) * 512;
+      src = cmp_kv + static_cast<long long>(crow[kidx - qk.nwin]) * 512;
     }
     const unsigned long long a = reinterpret_cast<unsigned long long>(src);
     const uint32_t a_lo = static_cast<uint32_t>(a), a_hi = static_cast<uint32_t>(a >> 32);
@@ -353,7 +383,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const float l_tot = quad_sum(l_run);
   float* inv_h = alpha_h;  // reused: 1 / l of every head
   tile_barrier();          // every wavefront is done with the factors of the last tile
-  if (g == 0) inv_h[head] = 1.f / l_tot;
+  if (g == 0) inv_h[head] = bad ? __builtin_nanf("") : 1.f / l_tot;
   lds_barrier();           // all reads of the last tile are done; inv_h is visible
   // Stage the output through the (now idle) tile buffers so it leaves as one contiguous
   // 1 KiB head row per store instruction.  This wavefront holds dims [128 wave, +128) of
@@ -387,7 +417,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint4 v = *reinterpret_cast<const uint4*>(kt + h * kRowBytes + ((el ^ swz(h)) << 4));
     *reinterpret_cast<uint4*>(obase + hh * 512 + el * 8) = v;
   }
-  if (lse != nullptr && g == 0) lse[static_cast<long long>(i) * 64 + head] = m_run * kLn2 + logf(l_tot);
+  if (lse != nullptr && g == 0)
+    lse[static_cast<long long>(i) * 64 + head] = bad ? __builtin_nanf("") : m_run * kLn2 + logf(l_tot);
 }
 
 // ----------------------------------------------------------------------------- generic path
@@ -403,9 +434,10 @@ constexpr int kGenPerThread = kGenMaxHD / kThreads;
 template <typename T>
 __global__ __launch_bounds__(kThreads) void mla_fwd_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ ori_kv, const T* __restrict__ cmp_kv,
-    const int32_t* __restrict__ cmp_idx, int topk, int H, int d, const int32_t* __restrict__ cu_q,
-    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl,
-    int wr, const float* __restrict__ sinks, float scale, T* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ cmp_idx, int topk, int Tc, int H, int d, const int32_t* __restrict__ cu_q,
+    const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, const int32_t* __restrict__ residual, int B,
+    int global_start, int r, int wl, int wr, const float* __restrict__ sinks, float scale, T* __restrict__ out,
+    float* __restrict__ lse) {
   extern __shared__ float gdyn[];
   __shared__ int32_t crow[kMaxTopk];
   __shared__ uint32_t wsum[kWaves];
@@ -416,8 +448,9 @@ __global__ __launch_bounds__(kThreads) void mla_fwd_generic_kernel(
   float* al = l + H;              // [H]
   float* pv = al + H;             // [H]
   const int i = blockIdx.x, tid = threadIdx.x;
-  const QueryKeys qk = query_keys(i, cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, cmp_kv != nullptr, cmp_idx,
-                                  topk, crow, wsum);
+  bool bad;
+  const QueryKeys qk = query_keys(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, wl, wr, Tc, cmp_kv != nullptr,
+                                  cmp_idx, topk, crow, wsum, bad);
   const int hd = H * d;
   for (int e = tid; e < hd; e += kThreads) qs[e] = ld(q, static_cast<long long>(i) * hd + e);
   for (int h = tid; h < H; h += kThreads) {
@@ -465,10 +498,11 @@ __global__ __launch_bounds__(kThreads) void mla_fwd_generic_kernel(
 #pragma unroll
   for (int u = 0; u < kGenPerThread; ++u) {
     const int e = tid + u * kThreads;
-    if (e < hd) st(out, static_cast<long long>(i) * hd + e, acc[u] / l[e / d]);
+    if (e < hd) st(out, static_cast<long long>(i) * hd + e, bad ? __builtin_nanf("") : acc[u] / l[e / d]);
   }
   if (lse != nullptr)
-    for (int h = tid; h < H; h += kThreads) lse[static_cast<long long>(i) * H + h] = m[h] + logf(l[h]);
+    for (int h = tid; h < H; h += kThreads)
+      lse[static_cast<long long>(i) * H + h] = bad ? __builtin_nanf("") : m[h] + logf(l[h]);
 }
 
 }  // namespace
@@ -479,19 +513,19 @@ bool mla_shape_supported(int H, int d, int dtype) {
 }
 
 hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
-                             int topk, int Tq, int H, int d, int dtype, const int32_t* cu_q,
-                             const int32_t* cu_kv, const int32_t* cu_cmp, int B, int global_start, int r,
-                             int wl, int wr, const float* sinks, float scale, void* out, float* lse,
-                             hipStream_t s) {
+                             int topk, bool topk_rows, int Tq, int Tc, int H, int d, int dtype, const int32_t* cu_q,
+                             const int32_t* cu_kv, const int32_t* cu_cmp, const int32_t* residual, int B,
+                             int global_start, int r, int wl, int wr, const float* sinks, float scale, void* out,
+                             float* lse, hipStream_t s) {
   if (Tq <= 0) return hipSuccess;
   if (cmp_idx == nullptr) topk = 0;
   if (dtype == 1 && H == 64 && d == 512) {
     const unsigned grid = static_cast<unsigned>((Tq + 63) / 64) * 64u;  // whole runs of 8 queries x 8 XCDs
     auto kern = (topk <= 2 * kThreads) ? mla_fwd_h64_d512_kernel<2> : mla_fwd_h64_d512_kernel<kMaxTopk / kThreads>;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, Tq, cu_q,
-                       cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale * kLog2e,
-                       static_cast<uint16_t*>(out), lse);
+                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk,
+                       topk_rows ? 1 : 0, Tq, Tc, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, wl, wr, sinks,
+                       scale * kLog2e, static_cast<uint16_t*>(out), lse);
     return hipGetLastError();
   }
   const size_t lds = (static_cast<size_t>(H) * d + d + 4 * static_cast<size_t>(H)) * sizeof(float);
@@ -500,16 +534,17 @@ hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_
     if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
       return e;
     hipLaunchKernelGGL(k, dim3(Tq), dim3(kThreads), lds, s, static_cast<const uint16_t*>(q),
-                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, H, d,
-                       cu_q, cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale, static_cast<uint16_t*>(out),
-                       lse);
+                       static_cast<const uint16_t*>(ori_kv), static_cast<const uint16_t*>(cmp_kv), cmp_idx, topk, Tc,
+                       H, d, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, wl, wr, sinks, scale,
+                       static_cast<uint16_t*>(out), lse);
   } else {
     auto k = mla_fwd_generic_kernel<float>;
     if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
       return e;
     hipLaunchKernelGGL(k, dim3(Tq), dim3(kThreads), lds, s, static_cast<const float*>(q),
-                       static_cast<const float*>(ori_kv), static_cast<const float*>(cmp_kv), cmp_idx, topk, H, d, cu_q,
-                       cu_kv, cu_cmp, B, global_start, r, wl, wr, sinks, scale, static_cast<float*>(out), lse);
+                       static_cast<const float*>(ori_kv), static_cast<const float*>(cmp_kv), cmp_idx, topk, Tc, H, d,
+                       cu_q, cu_kv, cu_cmp, residual, B, global_start, r, wl, wr, sinks, scale,
+                       static_cast<float*>(out), lse);
   }
   return hipGetLastError();
 }

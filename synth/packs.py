@@ -170,19 +170,11 @@ def pack_from_lengths(name, lengths, *, seed=0, dtype="bf16", H=64, d=512, H_I=6
     if rng is None:
         rng = np.random.default_rng(seed)
     bf16 = dtype == "bf16"
-    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
-    total = int(cu[-1])
+    total = int(np.sum(lengths))
     a, b = q_rows if q_rows is not None else (0, total)
     kv_end = kv_rows if kv_rows is not None else total
     assert 0 <= a <= b <= kv_end <= total
-    # segments that start before the KV prefix end, truncated at it
-    nb = int(np.searchsorted(cu, kv_end, side="left"))
-    nb = max(nb, 1) if kv_end > 0 else 1
-    cu_kv = np.minimum(cu[:nb + 1], kv_end)
-    if len(cu_kv) < 2:
-        cu_kv = np.array([0, kv_end])
-    cu_q = np.clip(cu_kv - a, 0, b - a)
-    Tq, Tkv = b - a, kv_end
+    cu_q, cu_kv, a, Tq, Tkv = _segments(lengths, q_rows, kv_rows)
     if q_scale is None:
         q_scale = 1.0 / math.sqrt(d)
     if kv_scale is None:
@@ -197,12 +189,77 @@ def pack_from_lengths(name, lengths, *, seed=0, dtype="bf16", H=64, d=512, H_I=6
         k_I = _draw(rng, (Tkv, d_I), kI_scale, bf16)
         w = _draw(rng, (Tq, H_I), w_scale, bf16)
     sinks = rng.standard_normal(H, dtype=np.float32)
-    return Pack(name=name, dtype=dtype, cu_seqlens_q=cu_q.astype(np.int32),
-                cu_seqlens_kv=cu_kv.astype(np.int32), global_start=int(a), Tq=int(Tq), Tkv=int(Tkv),
+    return Pack(name=name, dtype=dtype, cu_seqlens_q=cu_q, cu_seqlens_kv=cu_kv, global_start=int(a), Tq=int(Tq),
+                Tkv=int(Tkv),
                 H=H, d=d, H_I=H_I if indexer else 0, d_I=d_I if indexer else 0, cmp_ratio=cmp_ratio,
                 ori_win_left=ori_win_left, ori_win_right=ori_win_right, topk=topk,
                 softmax_scale=float(softmax_scale), q=q, ori_kv=ori_kv, q_I=q_I, k_I=k_I, w=w,
                 sinks=sinks, seed=seed)
+
+
+@dataclasses.dataclass
+class Layout:
+    """The THD layout and geometry of a workload, without its tensors (for callers that
+    draw the tensors elsewhere, e.g. on the device, with the same scales)."""
+    name: str
+    cu_seqlens_q: np.ndarray
+    cu_seqlens_kv: np.ndarray
+    global_start: int
+    Tq: int
+    Tkv: int
+    H: int = 64
+    d: int = 512
+    H_I: int = 64
+    d_I: int = 128
+    cmp_ratio: int = 4
+    ori_win_left: int = 127
+    ori_win_right: int = 0
+    topk: int = 512
+    q_scale: float = 512 ** -0.5
+    kv_scale: float = 512 ** -0.5
+    w_scale: float = 1.0 / 8
+    softmax_scale: float = 512 ** -0.5
+    indexer: bool = True
+
+    @property
+    def B(self) -> int:
+        return len(self.cu_seqlens_kv) - 1
+
+
+def _segments(lengths, q_rows=None, kv_rows=None):
+    """cu_seqlens_q, cu_seqlens_kv, global_start, Tq, Tkv of a pack: segments that start
+    before the KV prefix end, truncated at it; local query rows per segment."""
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    total = int(cu[-1])
+    a, b = q_rows if q_rows is not None else (0, total)
+    kv_end = kv_rows if kv_rows is not None else total
+    nb = int(np.searchsorted(cu, kv_end, side="left"))
+    nb = max(nb, 1) if kv_end > 0 else 1
+    cu_kv = np.minimum(cu[:nb + 1], kv_end)
+    if len(cu_kv) < 2:
+        cu_kv = np.array([0, kv_end])
+    cu_q = np.clip(cu_kv - a, 0, b - a)
+    return cu_q.astype(np.int32), cu_kv.astype(np.int32), int(a), int(b - a), int(kv_end)
+
+
+def workload_layout(name: str, seed: int = 0) -> Layout:
+    """Layout of one of the bf16 workloads below (single4k, pack16k, hca32k, cp32k),
+    drawn from the same generator stream as make_pack (segment lengths come first)."""
+    rng = np.random.default_rng(seed)
+    kw = {}
+    if name == "single4k":
+        seg = _segments([4096])
+    elif name == "pack16k":
+        seg = _segments(_lengths_pack16k(rng))
+    elif name == "hca32k":
+        seg = _segments(_lengths_hca32k(rng))
+        kw = dict(cmp_ratio=128, indexer=False, H_I=0, d_I=0)
+    elif name == "cp32k":
+        seg = _segments(_lengths_cp(rng), q_rows=(65536, 98304), kv_rows=98304)
+    else:
+        raise KeyError(name)
+    cu_q, cu_kv, gs, Tq, Tkv = seg
+    return Layout(name=name, cu_seqlens_q=cu_q, cu_seqlens_kv=cu_kv, global_start=gs, Tq=Tq, Tkv=Tkv, **kw)
 
 
 def _tiny(seed):

@@ -145,6 +145,40 @@ def assert_out_close(got, ref, fp32=False, what="out"):
     return msg
 
 
+class OutClose:
+    """assert_out_close over an output compared chunk by chunk (same bounds, computed
+    from running sums), so a full-size output never has to sit in float64 whole."""
+
+    def __init__(self, what="out"):
+        self.what = what
+        self.n = 0
+        self.mx = self.sum_abs = self.sum_sq = self.ref_sq = self.ref_inf = 0.0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        d = np.abs(got - ref)
+        self.n += d.size
+        self.mx = max(self.mx, float(d.max()) if d.size else 0.0)
+        self.sum_abs += float(d.sum())
+        self.sum_sq += float((d * d).sum())
+        self.ref_sq += float((ref * ref).sum())
+        self.ref_inf = max(self.ref_inf, float(np.abs(ref).max()) if ref.size else 0.0)
+
+    def check(self, fp32=False):
+        mean = self.sum_abs / max(self.n, 1)
+        l2 = math.sqrt(self.sum_sq) / max(math.sqrt(self.ref_sq), 1e-300)
+        msg = (f"{self.what}: max|d|={self.mx:.3e} mean|d|={mean:.3e} |ref|inf={self.ref_inf:.3e} "
+               f"relL2={l2:.3e} over {self.n} values")
+        assert self.mx <= OUT_MAX_ABS, msg
+        assert mean <= OUT_MEAN_ABS, msg
+        assert self.mx <= OUT_REL_INF * self.ref_inf, msg
+        assert l2 <= OUT_REL_L2, msg
+        if fp32:
+            assert self.mx <= OUT_F32_MAX_ABS, msg
+        return msg
+
+
 def oracle_attention(pack, tabs, queries, cmp_kv, cmp_idx_rows=None, mode=None):
     """Oracle sparse MLA for `queries` with the given compressed rows and selection."""
     if mode is None:

@@ -101,15 +101,16 @@ def test_compress_learned_accepts_empty_streams():
 
 
 def _idx(**kw):
-    a = dict(q=FAKE, w=FAKE, k=FAKE, Tq=8, H_I=64, d_I=128, dtype=1, cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE, B=1,
-             gs=0, r=4, maxlen=8, topk=512, idx=FAKE, sc=None, stream=None)
+    a = dict(q=FAKE, w=FAKE, k=FAKE, Tq=8, Tc=2, H_I=64, d_I=128, dtype=1, cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE,
+             res=None, B=1, gs=0, r=4, maxlen=8, topk=512, idx=FAKE, sc=None, stream=None)
     a.update(kw)
     return LIB.csa_indexer_topk(*a.values())
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), EINVAL), (dict(idx=None), EINVAL), (dict(topk=0), EINVAL), (dict(B=0), EINVAL),
-    (dict(maxlen=-1), EINVAL), (dict(dtype=3), EINVAL), (dict(topk=4096), EUNSUP),
+    (dict(maxlen=-1), EINVAL), (dict(dtype=3), EINVAL), (dict(Tc=-1), EINVAL), (dict(k=None), EINVAL),
+    (dict(topk=4096), EUNSUP),
     (dict(maxlen=4 * 40000), EUNSUP), (dict(H_I=128, d_I=128), EUNSUP), (dict(H_I=2, d_I=12, dtype=0), EUNSUP),
 ])
 def test_indexer_rejects(kw, code):
@@ -117,9 +118,9 @@ def test_indexer_rejects(kw, code):
 
 
 def _mla(**kw):
-    a = dict(q=FAKE, kv=FAKE, ckv=FAKE, cidx=FAKE, topk=512, Tq=8, Tkv=8, H=64, d=512, dtype=1, cu_q=FAKE,
-             cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, wl=127, wr=0, sinks=None, scale=0.04, out=FAKE, lse=None,
-             stream=None)
+    a = dict(q=FAKE, kv=FAKE, ckv=FAKE, cidx=FAKE, topk=512, kind=1, Tq=8, Tkv=8, Tc=2, H=64, d=512, dtype=1,
+             cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE, res=None, B=1, gs=0, r=4, wl=127, wr=0, sinks=None, scale=0.04,
+             out=FAKE, lse=None, stream=None)
     a.update(kw)
     return LIB.csa_sparse_mla_fwd(*a.values())
 
@@ -127,6 +128,7 @@ def _mla(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), EINVAL), (dict(out=None), EINVAL), (dict(ckv=None), EINVAL), (dict(topk=0), EINVAL),
     (dict(ckv=FAKE, cu_cmp=None), EINVAL), (dict(B=0), EINVAL), (dict(gs=1), EINVAL), (dict(wl=-1), EINVAL),
+    (dict(kind=2), EINVAL), (dict(kind=-1), EINVAL), (dict(Tc=-1), EINVAL),
     (dict(dtype=5), EINVAL), (dict(scale=0.0), EINVAL), (dict(scale=-0.04), EINVAL),
     (dict(wl=2**31 - 8), EINVAL), (dict(wr=2**31 - 8), EINVAL),
     (dict(scale=float("inf")), EINVAL), (dict(scale=float("nan")), EINVAL), (dict(topk=4096), EUNSUP),
@@ -202,8 +204,9 @@ def test_indexer_kl_grad_workspace_size_formula():
 
 
 def test_validate_layout_rejects_bad_arguments():
-    assert LIB.csa_validate_layout(None, FAKE, 1, 0, 0, 0, -1, None) == EINVAL
-    assert LIB.csa_validate_layout(FAKE, FAKE, 0, 0, 0, 0, -1, None) == EINVAL
+    assert LIB.csa_validate_layout(None, FAKE, 1, 0, 0, 0, -1, 0, None, None, None) == EINVAL
+    assert LIB.csa_validate_layout(FAKE, FAKE, 0, 0, 0, 0, -1, 0, None, None, None) == EINVAL
+    assert LIB.csa_validate_layout(FAKE, FAKE, 1, 0, 0, 0, -1, -1, None, None, None) == EINVAL
 
 
 def test_plan_rejects_learned_compressor_misuse_before_any_call():

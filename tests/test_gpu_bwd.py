@@ -1,9 +1,9 @@
 """GPU parity of the sparse-MLA backward (csa_sparse_mla_bwd) against the fp64 oracle.
 
 The forward runs on the GPU first (its out, lse, compressed rows and top-k lists feed
-the backward, as in training); a seeded bf16 dout drives both sides.  Small packs
-compare every output, including the row gradients (sums over all queries); the
-16k pack compares dq and the head-averaged probabilities on sampled queries.
+the backward, as in training); a seeded bf16 dout drives both sides.  Every pack, the 16k one included, compares
+every output: dq and the head-averaged probabilities of every query, and the row
+and sink gradients (sums over all queries).
 
 Tolerances (derived from the arithmetic): P and scale * dS enter the MFMA products
 rounded to bf16 (unit roundoff u = 2^-9), and D = dout . out uses the forward's bf16
@@ -20,7 +20,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_support import cpu, host_view, oracle_tables, run_pack, sample_queries, to_device
+from gpu_support import cpu, host_view, oracle_tables, run_pack, to_device
 from synth import make_pack, pack_from_lengths
 
 pytestmark = pytest.mark.gpu
@@ -165,19 +165,60 @@ def test_backward_is_deterministic_except_row_sums():
     np.testing.assert_allclose(a["d_ori_kv"], b["d_ori_kv"], rtol=1e-4, atol=1e-6)
 
 
-def test_backward_pack16k_sampled_queries():
-    """Full-size pack: dq and the probabilities of sampled queries (row gradients are
-    sums over every query and are covered by the small packs)."""
+class _CloseAcc:
+    """_close over a tensor compared in query chunks (same bounds, from running sums)."""
+
+    def __init__(self, what):
+        self.what, self.sq, self.ref_sq, self.mx, self.rinf = what, 0.0, 0.0, 0.0, 0.0
+
+    def add(self, got, ref):
+        got = np.asarray(got, dtype=np.float64)
+        ref = np.asarray(ref, dtype=np.float64)
+        diff = np.abs(got - ref)
+        self.sq += float((diff * diff).sum())
+        self.ref_sq += float((ref * ref).sum())
+        self.mx = max(self.mx, float(diff.max()) if diff.size else 0.0)
+        self.rinf = max(self.rinf, float(np.abs(ref).max()) if ref.size else 0.0)
+
+    def check(self):
+        l2 = float(np.sqrt(self.sq)) / max(float(np.sqrt(self.ref_sq)), 1e-300)
+        msg = f"{self.what}: max|d|={self.mx:.3e} |ref|inf={self.rinf:.3e} relL2={l2:.3e}"
+        print("   ", msg, flush=True)
+        assert l2 <= GRAD_REL_L2, msg
+        assert self.mx <= GRAD_REL_INF * self.rinf, msg
+
+
+def test_backward_pack16k_every_query():
+    """Full-size pack, every output against the oracle backward over all 16384 queries:
+    dq and the probabilities query by query, the row gradients and the sink gradient as
+    the sums over every query (the oracle runs in query chunks; its row gradients are
+    added up across the chunks)."""
     pack = make_pack("pack16k")
+    print(f"\n[case] pack16k: Tq={pack.Tq} -> forward on GPU", flush=True)
     plan = run_pack(pack)
     got, dout, attend_all, slots = _run_bwd(pack, plan, seed=101)
     tabs = oracle_tables(pack)
-    qs = sample_queries(pack, tabs, n=48)
-    ref = _oracle(pack, tabs, plan, dout, attend_all, slots, queries=qs)
-    _close(got["dq"][qs], ref["dq"], "dq (sampled)")
-    assert np.abs(got["ori_l1"][qs] - ref["ori_l1"]).max() <= L1_ABS
-    assert np.abs(got["cmp_l1"][qs] - ref["cmp_l1"]).max() <= L1_ABS
-    assert np.all(np.isfinite(got["d_ori_kv"])) and np.all(np.isfinite(got["d_cmp_kv"]))
+    dq = _CloseAcc("dq")
+    d_ori = d_cmp = d_s = None
+    l1_err = 0.0
+    step = 2048
+    for a in range(0, pack.Tq, step):
+        qs = list(range(a, min(a + step, pack.Tq)))
+        print(f"[case] pack16k: oracle backward, queries {a}..{qs[-1] + 1} of {pack.Tq}", flush=True)
+        ref = _oracle(pack, tabs, plan, dout, attend_all, slots, queries=qs)
+        dq.add(got["dq"][qs], ref["dq"])
+        l1_err = max(l1_err, float(np.abs(got["ori_l1"][qs] - ref["ori_l1"]).max()),
+                     float(np.abs(got["cmp_l1"][qs] - ref["cmp_l1"]).max()))
+        d_ori = ref["d_ori_kv"] if d_ori is None else d_ori + ref["d_ori_kv"]
+        d_cmp = ref["d_cmp_kv"] if d_cmp is None else d_cmp + ref["d_cmp_kv"]
+        d_s = ref["d_sinks"] if d_s is None else d_s + ref["d_sinks"]
+    dq.check()
+    print(f"    probabilities: max|d|={l1_err:.3e}", flush=True)
+    assert l1_err <= L1_ABS
+    _close(got["d_ori_kv"], d_ori, "d_ori_kv (sum over every query)")
+    tc = d_cmp.shape[0]
+    _close(got["d_cmp_kv"][:tc], d_cmp, "d_cmp_kv (sum over every query)")
+    _close(got["d_sinks"], d_s, "d_sinks (sum over every query)")
 
 
 def test_backward_empty_query_slice():

@@ -2,9 +2,9 @@
 
 Index tensors and compressed rows must be bit-exact.  Top-k sets must agree
 outside the 1e-3 score-tie band.  Attention outputs must meet the stated
-absolute bounds and the scale-aware relative bounds.  Small packs compare every
-query; the full-size workloads compare a sample of queries (random ones plus
-segment edges and top-k crossings) that the oracle computes one by one.
+absolute bounds and the scale-aware relative bounds.  Every query of every
+workload is compared, the full-size ones included (the oracle computes them one by
+one, in chunks that print their progress).
 """
 from __future__ import annotations
 
@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_support import (Decoded, assert_out_close, check_topk_row, cpu, host_view, oracle_attention,
-                         oracle_tables, run_pack, sample_queries, to_device, LSE_ABS)
+from gpu_support import (OutClose, assert_out_close, check_topk_row, cpu, host_view, oracle_attention,
+                         oracle_tables, run_pack, to_device, LSE_ABS)
 from synth import make_pack, pack_from_lengths
 
 pytestmark = pytest.mark.gpu
@@ -88,9 +88,18 @@ def result(name):
     return res
 
 
+CHUNK = 4096
+
+
 def _queries(res):
-    pack = res["pack"]
-    return list(range(pack.Tq)) if pack.Tq <= 3000 else sample_queries(pack, res["tabs"])
+    return list(range(res["pack"].Tq))
+
+
+def _chunks(qs, name, what):
+    for a in range(0, len(qs), CHUNK):
+        if len(qs) > CHUNK:
+            print(f"[case] {name}: {what} queries {a}..{min(a + CHUNK, len(qs))} of {len(qs)}", flush=True)
+        yield qs[a:a + CHUNK]
 
 
 @pytest.mark.parametrize("name", ALL)
@@ -135,14 +144,15 @@ def test_indexer_topk_sets(name):
     kc = _oracle_cmp(res, "k_I")
     qI, w = host_view(pack, "q_I"), host_view(pack, "w")
     flips = nsel = 0
-    for i in _queries(res):
-        lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
-        s = oracle.indexer_scores(qI[i], w[i], kc[lo:lo + nv]) if nv else np.zeros(0)
-        gsc = res["topk_score"][i] if nv > pack.topk else None
-        flips += check_topk_row(res["topk_idx"][i], lo, nv, s, pack.topk, gpu_scores=gsc)
-        nsel += nv > pack.topk
-        if nv and nv <= pack.topk:
-            np.testing.assert_allclose(res["topk_score"][i][:nv], s, rtol=1e-3, atol=1e-3)
+    for part in _chunks(_queries(res), name, "top-k sets,"):
+        for i in part:
+            lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
+            s = oracle.indexer_scores(qI[i], w[i], kc[lo:lo + nv]) if nv else np.zeros(0)
+            gsc = res["topk_score"][i] if nv > pack.topk else None
+            flips += check_topk_row(res["topk_idx"][i], lo, nv, s, pack.topk, gpu_scores=gsc)
+            nsel += nv > pack.topk
+            if nv and nv <= pack.topk:
+                np.testing.assert_allclose(res["topk_score"][i][:nv], s, rtol=1e-3, atol=1e-3)
     print(f"[case] {name}: {nsel} selecting queries checked, {flips} in-band swaps vs oracle order")
 
 
@@ -153,11 +163,15 @@ def test_attention_matches_oracle(name):
     qs = _queries(res)
     mode = oracle.layer_compress_mode(pack.cmp_ratio, int(tabs["cu_seqlens_cmp"][-1]))
     cmp_kv = _oracle_cmp(res, "ori_kv") if mode != oracle.NO_COMPRESS else None
-    rows = res["topk_idx"][qs] if mode == oracle.INDEXER else None
-    out, lse = oracle_attention(pack, tabs, qs, cmp_kv, rows, mode)
-    msg = assert_out_close(res["out"][qs], out, fp32=(pack.dtype == "f32"))
-    print(f"[case] {name}: {len(qs)} queries; {msg}")
-    assert np.abs(res["lse"][qs] - lse).max() <= LSE_ABS
+    acc, lse_err = OutClose(), 0.0
+    for part in _chunks(qs, name, "attention,"):
+        rows = res["topk_idx"][part] if mode == oracle.INDEXER else None
+        o, l = oracle_attention(pack, tabs, part, cmp_kv, rows, mode)
+        acc.add(res["out"][part], o)
+        lse_err = max(lse_err, float(np.abs(res["lse"][part] - l).max()))
+    msg = acc.check(fp32=(pack.dtype == "f32"))
+    print(f"[case] {name}: {len(qs)} queries; {msg}; max|lse diff|={lse_err:.3e}")
+    assert lse_err <= LSE_ABS
 
 
 @pytest.mark.parametrize("name", ["no_compress", "edges", "generic_bf16"])
@@ -170,10 +184,11 @@ def test_window_only_call_without_compressed_arrays(name):
     dt = torch.bfloat16 if pack.dtype == "bf16" else torch.float32
     out = torch.empty((pack.Tq, pack.H, pack.d), dtype=dt, device="cuda")
     lse = torch.empty((pack.Tq, pack.H), dtype=torch.float32, device="cuda")
-    s.csa_sparse_mla_fwd(to_device(pack.q), to_device(pack.ori_kv), None, None, 0, pack.Tq, pack.Tkv, pack.H,
-                         pack.d, torch.as_tensor(np.asarray(pack.cu_seqlens_q), dtype=torch.int32, device="cuda"),
-                         torch.as_tensor(np.asarray(pack.cu_seqlens_kv), dtype=torch.int32, device="cuda"), None, pack.B,
-                         pack.global_start, pack.cmp_ratio, pack.ori_win_left, pack.ori_win_right,
+    s.csa_sparse_mla_fwd(to_device(pack.q), to_device(pack.ori_kv), None, None, 0, s.CSA_IDX_ANY, pack.Tq, pack.Tkv,
+                         0, pack.H, pack.d,
+                         torch.as_tensor(np.asarray(pack.cu_seqlens_q), dtype=torch.int32, device="cuda"),
+                         torch.as_tensor(np.asarray(pack.cu_seqlens_kv), dtype=torch.int32, device="cuda"), None, None,
+                         pack.B, pack.global_start, pack.cmp_ratio, pack.ori_win_left, pack.ori_win_right,
                          to_device(pack.sinks), pack.softmax_scale, out, lse)
     torch.cuda.synchronize()
     qs = _queries(res)
@@ -290,19 +305,30 @@ def test_binding_refuses_short_tensors():
     q = torch.zeros((Tq, H, d), dtype=bf, device="cuda")
     kv = torch.zeros((Tq, d), dtype=bf, device="cuda")
     out = torch.zeros((Tq, H, d), dtype=bf, device="cuda")
+    A = s.CSA_IDX_ANY
     with pytest.raises(ValueError, match="q holds"):
-        s.csa_sparse_mla_fwd(q.view(-1)[:-1], kv, None, None, 0, Tq, Tq, H, d, cu, cu, None, 1, 0, 4, 127, 0, None,
-                             0.04, out)
+        s.csa_sparse_mla_fwd(q.view(-1)[:-1], kv, None, None, 0, A, Tq, Tq, 0, H, d, cu, cu, None, None, 1, 0, 4, 127,
+                             0, None, 0.04, out)
     with pytest.raises(ValueError, match="out holds"):
-        s.csa_sparse_mla_fwd(q, kv, None, None, 0, Tq, Tq, H, d, cu, cu, None, 1, 0, 4, 127, 0, None, 0.04,
+        s.csa_sparse_mla_fwd(q, kv, None, None, 0, A, Tq, Tq, 0, H, d, cu, cu, None, None, 1, 0, 4, 127, 0, None, 0.04,
                              out.view(-1)[: Tq * H * d - d])
     with pytest.raises(ValueError, match="cu_seqlens_kv holds"):
-        s.csa_sparse_mla_fwd(q, kv, None, None, 0, Tq, Tq, H, d, cu, cu[:1], None, 1, 0, 4, 127, 0, None, 0.04, out)
+        s.csa_sparse_mla_fwd(q, kv, None, None, 0, A, Tq, Tq, 0, H, d, cu, cu[:1], None, None, 1, 0, 4, 127, 0, None,
+                             0.04, out)
+    cu_cmp = torch.tensor([0, 16], dtype=i32, device="cuda")
+    ckv = torch.zeros((16, d), dtype=bf, device="cuda")
+    with pytest.raises(ValueError, match="cmp_kv holds"):  # fewer rows than the Tc the call names
+        s.csa_sparse_mla_fwd(q, kv, ckv[:15], None, 0, A, Tq, Tq, 16, H, d, cu, cu, cu_cmp, None, 1, 0, 4, 127, 0,
+                             None, 0.04, out)
+    with pytest.raises(ValueError, match="cmp_residual holds"):
+        s.csa_sparse_mla_fwd(q, kv, ckv, None, 0, A, Tq, Tq, 16, H, d, cu, cu, cu_cmp, cu_cmp[:0], 1, 0, 4, 127, 0,
+                             None, 0.04, out)
     qI = torch.zeros((Tq, 64, 128), dtype=bf, device="cuda")
     w = torch.zeros((Tq, 64), dtype=bf, device="cuda")
     kI = torch.zeros((16, 128), dtype=bf, device="cuda")
-    cu_cmp = torch.tensor([0, 16], dtype=i32, device="cuda")
     idx = torch.zeros((Tq, 8), dtype=i32, device="cuda")
     with pytest.raises(ValueError, match="topk_idx holds"):
-        s.csa_indexer_topk(qI, w, kI, Tq, 64, 128, cu, cu, cu_cmp, 1, 0, 4, 64, 16, idx)
+        s.csa_indexer_topk(qI, w, kI, Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 16, idx)
+    with pytest.raises(ValueError, match="k_I_cmp holds"):
+        s.csa_indexer_topk(qI, w, kI[:15], Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 8, idx)
     torch.cuda.synchronize()
