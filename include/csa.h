@@ -337,6 +337,27 @@ int csa_indexer_kl_grad(const void* q_I, const void* w, const void* k_I_cmp, con
                         float* loss, void* workspace, int64_t workspace_bytes, csa_stream_t stream);
 
 /*
+ * csa_indexer_kl_grad_noalloc - csa_indexer_kl_grad without a caller workspace and
+ * without any device allocation, for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and errors as csa_indexer_kl_grad, minus workspace and
+ * workspace_bytes.  The workspace is a device array the library holds: 64 MiB
+ * (CSA_KL_NOALLOC_SCRATCH_BYTES) on every GPU the call runs on, from the first call
+ * on that GPU until the process ends.  A call needing more,
+ * Tq * (4 topk + 2 floor(max_seqlen_kv / cmp_ratio)) bytes > 64 MiB, fails with
+ * CSA_EINVAL before any launch.  All calls on one GPU share that array: calls that
+ * overlap on one GPU (e.g. on two streams) race and give undefined results.
+ */
+#define CSA_KL_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int csa_indexer_kl_grad_noalloc(const void* q_I, const void* w, const void* k_I_cmp, const int32_t* cmp_idx,
+                                const float* attn_l1, int32_t topk, int32_t Tq, int32_t Tc, int32_t H_I, int32_t d_I,
+                                int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
+                                int32_t max_seqlen_kv, float loss_scale, void* d_q_I, float* d_w, float* d_k_I_cmp,
+                                float* loss, csa_stream_t stream);
+
+/*
  * csa_validate_layout - synchronous debug check of a THD layout held in device
  * memory: cu_seqlens_kv starts at 0, is non-decreasing and ends at Tkv;
  * cu_seqlens_q equals clamp(cu_seqlens_kv - global_start, 0, Tq); and the longest

@@ -38,6 +38,8 @@ SIGNATURES = {
     "csa_indexer_kl_grad_workspace_bytes": [_I, _I, _I, _I],
     "csa_indexer_kl_grad": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                             _P, _P, _P, _P, _P, C.c_int64, _P],
+    "csa_indexer_kl_grad_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I,
+                                    C.c_float, _P, _P, _P, _P, _P],
     "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
 }
 RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64,
@@ -229,6 +231,22 @@ def csa_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, H_I, d_
         B, global_start, cmp_ratio, max_seqlen_kv, float(loss_scale), _ptr(d_q_I, "d_q_I", dt, need=nq),
         _ptr(d_w, "d_w", f32, need=Tq * H_I), _ptr(d_k_I_cmp, "d_k_I_cmp", f32, True, Tc * d_I),
         _ptr(loss, "loss", f32, True, Tq), _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
+
+
+def csa_indexer_kl_grad_noalloc(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, H_I, d_I, cu_seqlens_q,
+                                cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, max_seqlen_kv, loss_scale,
+                                d_q_I, d_w, d_k_I_cmp, loss=None, stream=None):
+    i32, f32 = torch.int32, torch.float32
+    dt = q_I.dtype
+    nq = Tq * H_I * d_I
+    _check(LIB.csa_indexer_kl_grad_noalloc(
+        _ptr(q_I, "q_I", need=nq), _ptr(w, "w", dt, need=Tq * H_I), _ptr(k_I_cmp, "k_I_cmp", dt, True, Tc * d_I),
+        _ptr(cmp_idx, "cmp_idx", i32, need=Tq * topk), _ptr(attn_l1, "attn_l1", f32, need=Tq * topk), topk, Tq, Tc,
+        H_I, d_I, _dtype_code(q_I), _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1),
+        _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1), _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1),
+        B, global_start, cmp_ratio, max_seqlen_kv, float(loss_scale), _ptr(d_q_I, "d_q_I", dt, need=nq),
+        _ptr(d_w, "d_w", f32, need=Tq * H_I), _ptr(d_k_I_cmp, "d_k_I_cmp", f32, True, Tc * d_I),
+        _ptr(loss, "loss", f32, True, Tq), _stream(stream)))
 
 
 def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, max_seqlen_kv=-1, cmp_ratio=0,

@@ -277,6 +277,39 @@ int csa_indexer_kl_grad(const void* q_I, const void* w, const void* k_I_cmp, con
                     "csa_indexer_kl_grad");
 }
 
+int csa_indexer_kl_grad_noalloc(const void* q_I, const void* w, const void* k_I_cmp, const int32_t* cmp_idx,
+                                const float* attn_l1, int32_t topk, int32_t Tq, int32_t Tc, int32_t H_I, int32_t d_I,
+                                int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
+                                int32_t max_seqlen_kv, float loss_scale, void* d_q_I, float* d_w, float* d_k_I_cmp,
+                                float* loss, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp || (Tc > 0 && (!k_I_cmp || !d_k_I_cmp)) ||
+      (Tq != 0 && (!q_I || !w || !cmp_idx || !attn_l1 || !d_q_I || !d_w)))
+    return fail(CSA_EINVAL, "csa_indexer_kl_grad_noalloc: NULL pointer");
+  if (B < 1 || Tq < 0 || Tc < 0 || H_I < 1 || d_I < 1 || topk < 1 || cmp_ratio < 1 || global_start < 0 ||
+      max_seqlen_kv < 0)
+    return fail(CSA_EINVAL, "csa_indexer_kl_grad_noalloc: invalid size or parameter");
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_indexer_kl_grad_noalloc: unknown dtype %d", dtype);
+  if (topk > kMaxTopk)
+    return fail(CSA_EUNSUPPORTED, "csa_indexer_kl_grad_noalloc: topk %d > %d", topk, kMaxTopk);
+  if (!csa::kl_shape_supported(H_I, d_I, dtype))
+    return fail(CSA_EUNSUPPORTED, "csa_indexer_kl_grad_noalloc: no kernel for H_I=%d d_I=%d dtype=%d", H_I, d_I,
+                dtype);
+  const int nvis_cap = max_seqlen_kv / cmp_ratio;
+  const size_t need = csa::kl_workspace_bytes(Tq, topk, nvis_cap);
+  if (need > csa::kKlScratchBytes)
+    return fail(CSA_EINVAL, "csa_indexer_kl_grad_noalloc: the call needs %zu bytes of scratch, more than the %zu "
+                "the library holds (Tq * (4 topk + 2 floor(max_seqlen_kv / cmp_ratio)) must stay within it)",
+                need, csa::kKlScratchBytes);
+  void* ws = nullptr;
+  if (const int st = hip_status(csa::kl_scratch(&ws), "csa_indexer_kl_grad_noalloc"); st != CSA_OK) return st;
+  return hip_status(csa::launch_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, cu_seqlens_q,
+                                                cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio,
+                                                max_seqlen_kv, loss_scale, d_q_I, d_w, d_k_I_cmp, loss, nvis_cap, ws,
+                                                static_cast<hipStream_t>(stream)),
+                    "csa_indexer_kl_grad_noalloc");
+}
+
 int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t B, int32_t Tq,
                         int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv, int32_t cmp_ratio,
                         const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, csa_stream_t stream) {

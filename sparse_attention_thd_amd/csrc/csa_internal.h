@@ -47,6 +47,10 @@ hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_
                                   int nvis_cap, void* workspace, hipStream_t s);
 bool kl_shape_supported(int H_I, int d_I, int dtype);
 size_t kl_workspace_bytes(int Tq, int topk, int nvis_cap);
+// Library-held workspace of csa_indexer_kl_grad_noalloc: its device address on the
+// current device (looked up once per device).
+constexpr size_t kKlScratchBytes = size_t(64) << 20;
+hipError_t kl_scratch(void** ptr);
 
 hipError_t launch_compress_learned(const void* x, int Tkv, int D, const void* wkv, const void* wgate,
                                    const float* ape, int hd, int overlap, const int32_t* cu_kv,

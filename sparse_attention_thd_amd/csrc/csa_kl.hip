@@ -19,6 +19,8 @@
 //             registers and sweeps a chunk of 128 queries, forming u = q . K^T and
 //             d_k^T += q^T . M per query (q staged in LDS), then adds its tile to the
 //             float32 gradient once.
+#include <mutex>
+
 #include "csa_common.h"
 #include "csa_internal.h"
 #include "csa_tile.h"
@@ -538,6 +540,37 @@ __global__ void kl_zero_kernel(float* __restrict__ p, long long n) {
 bool kl_shape_supported(int H_I, int d_I, int dtype) { return dtype == 1 && H_I == 64 && d_I == 128; }
 
 size_t kl_workspace_bytes(int Tq, int topk, int nvis_cap) { return kl_ws_bytes(Tq, topk, nvis_cap); }
+
+// ---------------------------------------------------------------- library-held scratch
+
+// The workspace of the allocation-free entry point: a file-scope device array that
+// every GPU the library runs on holds from the first use until the process ends.  The
+// query kernel writes every slot the d_k kernel reads, so no clearing is needed.  All
+// calls on one GPU share it: calls that overlap on one GPU (on different streams)
+// race.  In host code the array's name is a host-side stand-in, never a device
+// address: kernels get the pointer hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kKlScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t kl_scratch(void** ptr) {
+  int dev = 0;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = (g_scratch_err[dev] == hipSuccess) ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_cmp, const int32_t* cmp_idx,
                                   const float* attn_l1, int topk, int Tq, int Tc, const int32_t* cu_q,

@@ -195,6 +195,31 @@ def test_indexer_kl_grad_rejects(kw, code):
     assert _kl(**kw) == code
 
 
+def _kl_noalloc(**kw):
+    a = dict(q=FAKE, w=FAKE, k=FAKE, cidx=FAKE, p=FAKE, topk=512, Tq=8, Tc=2, H=64, d=128, dtype=1, cu_q=FAKE,
+             cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, maxlen=8, scale=1.0, dq=FAKE, dw=FAKE, dk=FAKE, loss=None,
+             stream=None)
+    a.update(kw)
+    return LIB.csa_indexer_kl_grad_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), EINVAL), (dict(cidx=None), EINVAL), (dict(p=None), EINVAL), (dict(dq=None), EINVAL),
+    (dict(dk=None), EINVAL), (dict(topk=0), EINVAL), (dict(B=0), EINVAL), (dict(r=0), EINVAL),
+    (dict(Tq=40000, topk=512), EINVAL),                  # 40000 * 2048 B of slot gradients > 64 MiB
+    (dict(Tq=16384, maxlen=1 << 30), EINVAL),            # the visible-row map alone > 64 MiB
+    (dict(topk=4096), EUNSUP), (dict(H=16), EUNSUP), (dict(dtype=0), EUNSUP),
+])
+def test_indexer_kl_grad_noalloc_rejects(kw, code):
+    assert _kl_noalloc(**kw) == code
+    assert "csa_indexer_kl_grad_noalloc" in lib_mod.csa_last_error()
+
+
+def test_indexer_kl_grad_noalloc_limit_covers_the_16k_pack():
+    # the 16384-token pack (longest segment 4039 rows, top-512) fits the 64 MiB the library holds
+    assert LIB.csa_indexer_kl_grad_workspace_bytes(16384, 512, 4039, 4) <= 64 << 20
+
+
 def test_indexer_kl_grad_workspace_size_formula():
     # per query: topk float32 slot gradients + a 2 B map entry per visible compressed row
     assert LIB.csa_indexer_kl_grad_workspace_bytes(10, 512, 4096, 4) == 10 * (512 * 4 + 2 * 1024)
