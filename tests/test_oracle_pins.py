@@ -212,6 +212,66 @@ def test_indexer_single_head_is_a_stable_sort(seed):
         assert list(idx[i][idx[i] >= 0]) == sorted(lo + int(j) for j in best)
 
 
+@pytest.mark.parametrize("h0", range(3))
+def test_indexer_one_hot_weights_rank_by_that_head_alone(h0):
+    """Weights e_h0 reduce the head-weighted sum to head h0's ReLU logits: the kept rows
+    are the stable top-k of ReLU(q[h0] . k) (the other heads' q must not matter)."""
+    tabs, qI, _, kc = _indexer_case(20 + h0, H_I=3, maxlen=90)
+    w = np.zeros((len(qI), 3))
+    w[:, h0] = 1.0
+    noise = np.random.default_rng(5).standard_normal(qI.shape)
+    qI2 = qI.copy()
+    qI2[:, [h for h in range(3) if h != h0]] = noise[:, [h for h in range(3) if h != h0]]
+    topk = 4
+    a, sa = oracle.indexer_topk(qI, w, kc, tabs, topk=topk)
+    b, _ = oracle.indexer_topk(qI2, w, kc, tabs, topk=topk)
+    np.testing.assert_array_equal(a, b)
+    for i in range(len(a)):
+        lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
+        s = np.array([max(float(np.dot(kc[lo + j], qI[i, h0])), 0.0) for j in range(nv)])
+        best = np.argsort(-s, kind="stable")[:topk]
+        kept = a[i][a[i] >= 0]
+        assert list(kept) == sorted(lo + int(j) for j in best)
+        # the reported score of a kept row is that head's ReLU logit itself (weight 1)
+        np.testing.assert_allclose(sa[i][:len(kept)], s[kept - lo], rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_negated_weights_reverse_the_order_of_positive_logits():
+    """With every logit of the weighted head positive, -w ranks the rows in the reverse
+    order: the kept rows are the topk smallest logits (ties to the lower row)."""
+    tabs, qI, _, kc = _indexer_case(30, H_I=2, maxlen=90)
+    qI, kc = np.abs(qI), np.abs(kc)          # positive vectors: every logit > 0
+    w = np.zeros((len(qI), 2))
+    w[:, 1] = -0.5
+    topk = 3
+    idx, _ = oracle.indexer_topk(qI, w, kc, tabs, topk=topk)
+    for i in range(len(idx)):
+        lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
+        logit = kc[lo:lo + nv] @ qI[i, 1]
+        assert np.all(logit > 0)
+        worst = np.argsort(logit, kind="stable")[:topk]
+        assert list(idx[i][idx[i] >= 0]) == sorted(lo + int(j) for j in worst)
+
+
+def test_indexer_scores_are_linear_in_the_head_weights():
+    """score(w) = sum_h w_h score(e_h): the weighted sum over heads, each head's term
+    taken from the one-hot score (all candidates kept, so every score is reported)."""
+    tabs, qI, w, kc = _indexer_case(40, H_I=3, maxlen=50)
+    topk = 64
+    _, full = oracle.indexer_topk(qI, w, kc, tabs, topk=topk)
+    parts = []
+    for h in range(3):
+        e = np.zeros_like(w)
+        e[:, h] = 1.0
+        parts.append(oracle.indexer_topk(qI, e, kc, tabs, topk=topk)[1])
+    for i in range(len(full)):
+        nv = int(tabs["q_cmp_nvis"][i])
+        combo = sum(w[i, h] * parts[h][i][:nv] for h in range(3))
+        np.testing.assert_allclose(full[i][:nv], combo, rtol=1e-12, atol=1e-12)
+        for h in range(3):
+            assert np.all(parts[h][i][:nv] >= 0)   # each head's term is a ReLU
+
+
 def test_indexer_scores_only_own_segment_packing_invariant():
     tabs, qI, w, kc = _indexer_case(7, nseg=4, maxlen=70)
     idx, sc = oracle.indexer_topk(qI, w, kc, tabs, topk=4)
