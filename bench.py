@@ -313,7 +313,8 @@ def time_forward(plan, inputs, steps, warmup):
         if plan.topk_idx is not None:
             _lib.csa_indexer_topk(inputs["q_I"], inputs["w"], plan.k_I_cmp, L.Tq, plan.Tc_cap, plan.H_I, plan.d_I,
                                   L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, plan.cmp_residual, L.B,
-                                  L.global_start, plan.r, L.max_seqlen_kv, plan.topk, plan.topk_idx, None)
+                                  L.global_start, plan.r, L.max_seqlen_kv, plan.topk, plan.topk_idx, None,
+                                  plan.indexer_ws)
 
     def mla():
         cmp_idx = plan.topk_idx

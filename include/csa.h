@@ -172,21 +172,26 @@ int csa_compress_learned(const void* x, int32_t Tkv, int32_t D, int32_t dtype, c
  * fixes that range, so the value must equal len_b mod r (what csa_build_indices
  * writes); a query whose segment disagrees gets an all -1 row (and NaN scores), so
  * a stale residual shows in the output instead of passing silently.
- * The scores live in on-chip memory: the call needs no workspace.
- * `max_seqlen_kv` must bound every segment length; it sizes that on-chip score
- * storage (floor(max_seqlen_kv / r) candidates per query).  Segments longer than
- * it give unspecified (but in-bounds) results.
+ * workspace: device memory of at least csa_indexer_topk_workspace_bytes(Tq,
+ * max_seqlen_kv, cmp_ratio) = Tq * floor(max_seqlen_kv / r) * 4 bytes, owned by the caller:
+ * the order-preserving keys of the scores, written by a scoring pass and read by the
+ * selection (no memory is allocated; nothing in it needs clearing).
+ * `max_seqlen_kv` must bound every segment length; it sizes the workspace rows (and,
+ * for the small shapes, the on-chip key storage): floor(max_seqlen_kv / r) candidates
+ * per query.  Segments longer than it give unspecified (but in-bounds) results.
  * Errors: EINVAL for NULL required pointers, B < 1, Tq < 0, Tc < 0, H_I < 1, d_I < 1,
- * topk < 1, cmp_ratio < 1, max_seqlen_kv < 0; EUNSUPPORTED for
- * floor(max_seqlen_kv / r) > 32768 candidates, topk > 2048, or a shape other
+ * topk < 1, cmp_ratio < 1, max_seqlen_kv < 0, a missing or short workspace; EUNSUPPORTED
+ * for floor(max_seqlen_kv / r) > 32768 candidates, topk > 2048, or a shape other
  * than (H_I, d_I) = (64, 128) bf16 or H_I * d_I <= 8192 with d_I % 8 == 0.
  */
+int64_t csa_indexer_topk_workspace_bytes(int32_t Tq, int32_t max_seqlen_kv, int32_t cmp_ratio);
 int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp,
                      int32_t Tq, int32_t Tc, int32_t H_I, int32_t d_I, int32_t dtype,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                      const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, int32_t B,
                      int32_t global_start, int32_t cmp_ratio, int32_t max_seqlen_kv, int32_t topk,
-                     int32_t* topk_idx, float* topk_score, csa_stream_t stream);
+                     int32_t* topk_idx, float* topk_score, void* workspace, int64_t workspace_bytes,
+                     csa_stream_t stream);
 
 /* How the rows of a cmp_idx argument were formed (csa_sparse_mla_fwd). */
 enum {

@@ -29,7 +29,9 @@ SIGNATURES = {
     "csa_build_indices": [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P],
     "csa_compress": [_P, _I, _I, _I, _P, _P, _I, _I, _P, _I, _P],
     "csa_compress_learned": [_P, _I, _I, _I, _P, _P, _P, _I, _I, _P, _P, _I, _I, _P, _I, _P],
-    "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P],
+    "csa_indexer_topk_workspace_bytes": [_I, _I, _I],
+    "csa_indexer_topk": [_P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, C.c_int64,
+                         _P],
     "csa_sparse_mla_fwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P,
                            C.c_float, _P, _P, _P],
     "csa_sparse_mla_bwd_workspace_bytes": [_I, _I, _I, _P, _P, _I, _I, _I],
@@ -43,6 +45,7 @@ SIGNATURES = {
     "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
 }
 RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64,
+            "csa_indexer_topk_workspace_bytes": C.c_int64,
             "csa_indexer_kl_grad_workspace_bytes": C.c_int64}
 
 
@@ -149,17 +152,27 @@ def csa_compress_learned(x, Tkv, D, wkv, wgate, ape, hd, overlap, cu_seqlens_kv,
                                     _ptr(x_cmp, "x_cmp", x.dtype, need=Tc_cap * hd), Tc_cap, _stream(stream)))
 
 
+def csa_indexer_topk_workspace_bytes(Tq, max_seqlen_kv, cmp_ratio):
+    n = LIB.csa_indexer_topk_workspace_bytes(Tq, max_seqlen_kv, cmp_ratio)
+    if n < 0:
+        raise CsaError(CSA_EINVAL, "csa_indexer_topk_workspace_bytes: invalid arguments")
+    return int(n)
+
+
 def csa_indexer_topk(q_I, w, k_I_cmp, Tq, Tc, H_I, d_I, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, cmp_residual,
-                     B, global_start, cmp_ratio, max_seqlen_kv, topk, topk_idx, topk_score=None, stream=None):
+                     B, global_start, cmp_ratio, max_seqlen_kv, topk, topk_idx, topk_score=None, workspace=None,
+                     stream=None):
     i32 = torch.int32
     dt = q_I.dtype
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(LIB.csa_indexer_topk(
         _ptr(q_I, "q_I", need=Tq * H_I * d_I), _ptr(w, "w", dt, need=Tq * H_I),
         _ptr(k_I_cmp, "k_I_cmp", dt, Tc == 0, Tc * d_I), Tq, Tc, H_I, d_I, _dtype_code(q_I),
         _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
         _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1), _ptr(cmp_residual, "cmp_residual", i32, True, B),
         B, global_start, cmp_ratio, max_seqlen_kv, topk, _ptr(topk_idx, "topk_idx", i32, need=Tq * topk),
-        _ptr(topk_score, "topk_score", torch.float32, True, Tq * topk), _stream(stream)))
+        _ptr(topk_score, "topk_score", torch.float32, True, Tq * topk), _ptr(workspace, "workspace", optional=True),
+        ws_bytes, _stream(stream)))
 
 
 def csa_sparse_mla_fwd(q, ori_kv, cmp_kv, cmp_idx, topk, cmp_idx_kind, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv,

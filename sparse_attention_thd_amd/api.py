@@ -108,12 +108,14 @@ class CsaPlan:
         self.q_cmp_lo = torch.empty(Tq, **i32)
         self.q_cmp_nvis = torch.empty(Tq, **i32)
         self.cmp_group = torch.full((self.Tc_cap,), -1, **i32)
-        self.cmp_kv = self.k_I_cmp = self.topk_idx = self.topk_score = None
+        self.cmp_kv = self.k_I_cmp = self.topk_idx = self.topk_score = self.indexer_ws = None
         if self.mode != LayerCompressMode.NO_COMPRESS:
             self.cmp_kv = torch.zeros((self.Tc_cap, d), dtype=dtype, device=dev)
         if self.mode == LayerCompressMode.INDEXER:
             self.k_I_cmp = torch.zeros((self.Tc_cap, d_I), dtype=dtype, device=dev)
             self.topk_idx = torch.empty((Tq, topk), **i32)
+            nb = _lib.csa_indexer_topk_workspace_bytes(Tq, layout.max_seqlen_kv, cmp_ratio)
+            self.indexer_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
             if return_topk_score:
                 self.topk_score = torch.empty((Tq, topk), dtype=torch.float32, device=dev)
         self.out = torch.empty((Tq, H, d), dtype=dtype, device=dev)
@@ -148,7 +150,7 @@ class CsaPlan:
                                   self.k_I_cmp, self.Tc_cap, stream)
             _lib.csa_indexer_topk(q_I, w, self.k_I_cmp, L.Tq, self.Tc_cap, self.H_I, self.d_I, L.cu_seqlens_q,
                                   L.cu_seqlens_kv, self.cu_seqlens_cmp, self.cmp_residual, L.B, L.global_start, self.r,
-                                  L.max_seqlen_kv, self.topk, self.topk_idx, self.topk_score, stream)
+                                  L.max_seqlen_kv, self.topk, self.topk_idx, self.topk_score, self.indexer_ws, stream)
             cmp_idx = self.topk_idx
         _lib.csa_sparse_mla_fwd(q, ori_kv, self.cmp_kv, cmp_idx, self.topk if cmp_idx is not None else 0,
                                 _lib.CSA_IDX_TOPK, L.Tq, L.Tkv, self.Tc_cap if self.cmp_kv is not None else 0, self.H,

@@ -114,11 +114,16 @@ int csa_compress_learned(const void* x, int32_t Tkv, int32_t D, int32_t dtype, c
                     "csa_compress_learned");
 }
 
+int64_t csa_indexer_topk_workspace_bytes(int32_t Tq, int32_t max_seqlen_kv, int32_t cmp_ratio) {
+  if (Tq < 0 || max_seqlen_kv < 0 || cmp_ratio < 1) return -1;
+  return static_cast<int64_t>(csa::indexer_workspace_bytes(Tq, max_seqlen_kv / cmp_ratio));
+}
+
 int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_t Tq, int32_t Tc, int32_t H_I,
                      int32_t d_I, int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
                      const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual, int32_t B, int32_t global_start,
                      int32_t cmp_ratio, int32_t max_seqlen_kv, int32_t topk, int32_t* topk_idx, float* topk_score,
-                     csa_stream_t stream) {
+                     void* workspace, int64_t workspace_bytes, csa_stream_t stream) {
   if (!cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp || (Tc > 0 && !k_I_cmp) ||
       (Tq != 0 && (!q_I || !w || !topk_idx)))
     return fail(CSA_EINVAL, "csa_indexer_topk: NULL pointer");
@@ -133,9 +138,13 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_
                 kMaxCandidates);
   if (!csa::indexer_shape_supported(H_I, d_I, dtype))
     return fail(CSA_EUNSUPPORTED, "csa_indexer_topk: no kernel for H_I=%d d_I=%d dtype=%d", H_I, d_I, dtype);
+  const int64_t need = static_cast<int64_t>(csa::indexer_workspace_bytes(Tq, cap));
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(CSA_EINVAL, "csa_indexer_topk: workspace of %lld bytes < %lld needed",
+                workspace ? static_cast<long long>(workspace_bytes) : 0LL, static_cast<long long>(need));
   return hip_status(csa::launch_indexer_topk(q_I, w, k_I_cmp, Tq, Tc, H_I, d_I, dtype, cu_seqlens_q, cu_seqlens_kv,
                                              cu_seqlens_cmp, cmp_residual, B, global_start, cmp_ratio, cap, topk,
-                                             topk_idx, topk_score, static_cast<hipStream_t>(stream)),
+                                             topk_idx, topk_score, workspace, static_cast<hipStream_t>(stream)),
                     "csa_indexer_topk");
 }
 

@@ -1,25 +1,27 @@
 // Lightning indexer + per-query top-k over the query's own segment.
 //
-// One workgroup (4 wavefronts) per query.  Queries with no more candidates than
-// top-k only write the ascending candidate list.  Otherwise every candidate is
-// scored into LDS as an order-preserving uint32 key, a 4-pass 8-bit radix select
-// finds the k-th largest key, and an ordered block scan emits the kept rows in
-// ascending order (exact ties go to the lower row).
+// Queries with no more candidates than top-k only write the ascending candidate list.
+// Otherwise every candidate gets an order-preserving uint32 key of its score, a 4-pass
+// 8-bit radix select finds the k-th largest key, and an ordered scan emits the kept rows
+// in ascending order (exact ties go to the lower row).
 //
-// Scoring paths:
-//   * (H_I, d_I) = (64, 128) bf16: v_mfma_f32_16x16x32_bf16 with the query's 64
-//     heads as M (register-resident A operand), 16 candidates as N (B operand
-//     loaded straight from global/L2), ReLU and head weighting on the fp32 C
-//     fragments, then a 4-lane-group reduction.
-//   * small shapes (H_I * d_I <= 8192, either dtype): scalar fp32 per candidate.
+// (H_I, d_I) = (64, 128) bf16: indexer_score_kernel, a workgroup of 8 wavefronts per 8
+// consecutive queries.  The queries of one segment share that segment's compressed keys,
+// staged through LDS in chunks of 64 rows (16 KiB, global_load_lds, XOR-swizzled 16-byte
+// chunks, three buffers) once for all of them.  Wavefront w scores query w:
+// v_mfma_f32_16x16x32_bf16 with the 64 indexer heads as M (q_I in registers), 16
+// candidates as N (conflict-free 16-byte LDS reads), ReLU and head weights on the fp32 C
+// fragments, a 4-lane-group sum; the keys go to the caller's workspace (one row of
+// floor(max_seqlen_kv / r) per query).  indexer_select_kernel then gives each query one
+// wavefront that selects from its keys with no workgroup barrier (wave_select_emit).
+// Small shapes (H_I * d_I <= 8192, either dtype): indexer_topk_kernel scores with scalar
+// fp32 straight into LDS and selects with the whole workgroup.
 #include "csa_common.h"
 #include "csa_internal.h"
+#include "csa_tile.h"
 
 namespace csa {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 
 struct SelectShared {
   uint32_t hist[256];
@@ -139,115 +141,14 @@ __device__ void score_generic(const T* __restrict__ q_I, const T* __restrict__ w
   }
 }
 
-// MFMA scoring, 64 indexer heads x 128 dims, bf16.
-__device__ void score_mfma_64x128(const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w,
-                                  const uint16_t* __restrict__ k_cmp, int i, int lo, int nv, uint32_t* keys) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  // A operand: q_I[i, 16*mb + n, 32*ks + 8*g + 0..7]
-  bf16x8 qa[4][4];
-  const uint16_t* qrow = q_I + static_cast<long long>(i) * 64 * 128;
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      qa[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (16 * mb + n) * 128 + 32 * ks + 8 * g);
-  // head weights for the C rows this lane holds: heads 16*mb + 4*g + j
-  float wv[4][4];
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wv[mb][j] = bf16_bits_to_f32(w[static_cast<long long>(i) * 64 + 16 * mb + 4 * g + j]);
-  const int nblk = (nv + 15) >> 4;
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const int c = 16 * jb + n;  // candidate of this lane's B column
-    bf16x8 kb[4];
-    if (c < nv) {
-      const uint16_t* krow = k_cmp + static_cast<long long>(lo + c) * 128;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks + 8 * g);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[ks] = bf16x8{};
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mb][ks], kb[ks], acc, 0, 0, 0);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) s += wv[mb][j] * fmaxf(acc[j], 0.f);
-    }
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
-    if (g == 0 && c < nv) keys[c] = float_order_key(s);
-  }
-}
-
-// MFMA scoring of two queries of one segment (same candidate rows) in one pass: every
-// 16-candidate block of keys is loaded once and multiplied by both queries' q (128
-// register rows), which halves the key bytes per MFMA of the vector-memory path.
-__device__ void score_mfma_64x128_pair(const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w,
-                                       const uint16_t* __restrict__ k_cmp, int i0, int lo, int nv0, int nv1,
-                                       uint32_t* keys0, uint32_t* keys1) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n = lane & 15, g = lane >> 4;
-  bf16x8 qa[2][4][4];
-  float wv[2][4][4];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const uint16_t* qrow = q_I + static_cast<long long>(i0 + e) * 64 * 128;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qa[e][mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (16 * mb + n) * 128 + 32 * ks + 8 * g);
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wv[e][mb][j] = bf16_bits_to_f32(w[static_cast<long long>(i0 + e) * 64 + 16 * mb + 4 * g + j]);
-  }
-  const int nvm = max(nv0, nv1);
-  const int nblk = (nvm + 15) >> 4;
-  for (int jb = wave; jb < nblk; jb += kWaves) {
-    const int c = 16 * jb + n;
-    bf16x8 kb[4];
-    if (c < nvm) {
-      const uint16_t* krow = k_cmp + static_cast<long long>(lo + c) * 128;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[ks] = *reinterpret_cast<const bf16x8*>(krow + 32 * ks + 8 * g);
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kb[ks] = bf16x8{};
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      float sc = 0.f;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[e][mb][ks], kb[ks], acc, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sc += wv[e][mb][j] * fmaxf(acc[j], 0.f);
-      }
-      sc += __shfl_xor(sc, 16, 64);
-      sc += __shfl_xor(sc, 32, 64);
-      if (g == 0 && c < (e ? nv1 : nv0)) (e ? keys1 : keys0)[c] = float_order_key(sc);
-    }
-  }
-}
-
 // Candidate range of local query i: rows [lo, lo + nv) of its segment b that are
 // causally complete, exist in the k_cmp buffer (Tc rows) and fit the score storage.
 // With a caller-held residual that disagrees with the segment length, nv = -1 (the
 // query's row is then written as all -1).
-__device__ __forceinline__ void candidate_range(int i, const int32_t* __restrict__ cu_q,
-                                                const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
-                                                const int32_t* __restrict__ residual, int B, int global_start, int r,
-                                                int cap, int Tc, int& lo, int& nv) {
+__device__ __forceinline__ int candidate_range(int i, const int32_t* __restrict__ cu_q,
+                                               const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
+                                               const int32_t* __restrict__ residual, int B, int global_start, int r,
+                                               int cap, int Tc, int& lo, int& nv) {
   const int b = segment_of(cu_q, B, i);
   const int s = cu_kv[b];
   const int p = global_start + i - s;
@@ -257,6 +158,7 @@ __device__ __forceinline__ void candidate_range(int i, const int32_t* __restrict
   v = min(v, Tc - lo);
   nv = max(0, min(v, cap));
   if (residual != nullptr && residual[b] != (cu_kv[b + 1] - s) % r) nv = -1;
+  return b;
 }
 
 // The row of a query whose segment's residual disagrees: no selection, NaN scores.
@@ -268,68 +170,459 @@ __device__ __forceinline__ void write_poisoned_row(int32_t* __restrict__ out_idx
   }
 }
 
-// (H_I, d_I) = (64, 128) bf16, two queries per workgroup: queries 2 x and 2 x + 1.
-// A query with no more candidates than top-k only writes its ascending list.  Two
-// selecting queries of one segment are scored in one pass (above); otherwise each is
-// scored alone.  The selections then run one after the other.
-__global__ __launch_bounds__(kThreads) void indexer_topk_pair_kernel(
-    const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp,
-    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
-    const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk, int Tq,
-    int32_t* __restrict__ idx, float* __restrict__ score) {
-  extern __shared__ uint32_t dyn[];  // two key arrays of cap entries
-  __shared__ SelectShared sh;
-  const int i0 = 2 * static_cast<int>(blockIdx.x);
-  const int tid = threadIdx.x;
-  const int nq = min(2, Tq - i0);
-  int lo[2] = {0, 0}, nv[2] = {0, 0};
-  bool heavy[2] = {false, false};
+constexpr int kSThreads = 512;             // fused workgroup: 8 wavefronts, one query each
+constexpr int kSWaves = kSThreads / 64;
+constexpr int kChunk = 64;                 // candidates per LDS chunk (64 rows of 256 B)
+constexpr int kStages = 3;                 // chunk buffers: loads run two chunks ahead
+constexpr int kRun = 4;                    // consecutive tiles per XCD run
+
+constexpr int kList = 768;  // per-wavefront LDS list of the keys in the threshold bin
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    if (e >= nq) break;
-    const int i = i0 + e;
-    candidate_range(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap, Tc, lo[e], nv[e]);
-    if (nv[e] < 0) {
-      write_poisoned_row(idx + static_cast<long long>(i) * topk, score ? score + static_cast<long long>(i) * topk : nullptr,
-                         topk);
-      nv[e] = 0;
-      continue;
-    }
-    heavy[e] = !(nv[e] <= topk && score == nullptr);
-    if (!heavy[e]) {
-      int32_t* out_idx = idx + static_cast<long long>(i) * topk;
-      for (int k = tid; k < topk; k += kThreads) out_idx[k] = (k < nv[e]) ? lo[e] + k : -1;
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
+// 256 LDS bins of one wavefront: the bin d that holds the kk-th largest entry (counting
+// from the top bin down) and the count of entries in the bins above it.  Lane l reads
+// bins 255 - 4 l .. 252 - 4 l, so lane order is descending bin order.
+__device__ __forceinline__ void wave_hist_find(const uint32_t* hist, uint32_t kk, uint32_t& digit, uint32_t& above) {
+  const int lane = threadIdx.x & 63;
+  uint32_t c[4], loc = 0;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    c[t] = hist[255 - 4 * lane - t];
+    loc += c[t];
+  }
+  uint32_t incl = loc;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  const uint32_t excl = incl - loc;
+  const bool here = excl < kk && incl >= kk;
+  int dsel = 0;
+  uint32_t ab = excl;
+  if (here) {
+    uint32_t run = excl;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (run + c[t] >= kk) {
+        dsel = 255 - 4 * lane - t;
+        ab = run;
+        break;
+      }
+      run += c[t];
     }
   }
-  if (!heavy[0] && !heavy[1]) return;
-  uint32_t* keys[2] = {dyn, dyn + cap};
-  if (heavy[0] && heavy[1] && lo[0] == lo[1]) {
-    score_mfma_64x128_pair(q_I, w, k_cmp, i0, lo[0], nv[0], nv[1], keys[0], keys[1]);
+  const int src = __ffsll(static_cast<long long>(__ballot(here))) - 1;
+  digit = static_cast<uint32_t>(__shfl(dsel, src, 64));
+  above = static_cast<uint32_t>(__shfl(static_cast<int>(ab), src, 64));
+}
+
+__device__ __forceinline__ void wave_hist_zero(uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) hist[64 * t + lane] = 0u;
+}
+
+// Bin of a key on the linear scale between fmin and fmax (scale = 256 / (fmax - fmin),
+// finite): the subtraction, the product and the truncation are each monotone, so the bin
+// never decreases with the key.
+__device__ __forceinline__ uint32_t linear_bin(uint32_t key, float fmin, float scale) {
+  const float x = (order_key_to_float(key) - fmin) * scale;
+  return static_cast<uint32_t>(min(max(static_cast<int>(x), 0), 255));
+}
+
+// Radix select over bits top..0 of the keys that have the given prefix in the bits above
+// top: the kk-th largest such key.  FROM_LIST: the m keys in list (LDS); otherwise the nv
+// keys in global memory that fall in linear bin `bsel` (bsel < 0: every key).
+template <bool FROM_LIST>
+__device__ uint32_t wave_radix_kth(const uint32_t* __restrict__ keys, int nv, const uint32_t* list, int m, int top,
+                                   uint32_t prefix, uint32_t& kk, int bsel, float fmin, float scale, uint32_t* hist) {
+  const int lane = threadIdx.x & 63;
+  uint32_t pmask = (top >= 31) ? 0u : ~((2u << top) - 1u);
+  prefix &= pmask;
+  while (top >= 0) {
+    const int w = min(8, top + 1);
+    const int shift = top - w + 1;
+    const uint32_t dmask = (1u << w) - 1u;
+    wave_hist_zero(hist);
+    const int n = FROM_LIST ? m : nv;
+    for (int j = lane; j < n; j += 64) {
+      const uint32_t k = FROM_LIST ? list[j] : keys[j];
+      bool in = (k & pmask) == prefix;
+      if (!FROM_LIST && bsel >= 0) in = in && linear_bin(k, fmin, scale) == static_cast<uint32_t>(bsel);
+      if (in) atomicAdd(&hist[(k >> shift) & dmask], 1u);
+    }
+    uint32_t d, ab;
+    wave_hist_find(hist, kk, d, ab);
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    kk -= ab;
+    top -= w;
+  }
+  return prefix;
+}
+
+// Select the topk largest of one query's nv > topk keys and write them ascending, exact
+// ties to the lower row, with this wavefront alone (no workgroup barrier), streaming the
+// keys (L2-resident after the first pass):
+//   1. min and max key;
+//   2. a 256-bin histogram linear in the score between them (scores cluster in a few
+//      binades, so bins of the raw key bits would collide on every LDS atomic): the bin of
+//      the topk-th largest key and the count above it;
+//   3. the keys of that bin go to an LDS list (when they fit), and a radix select from
+//      their first differing bit finds the threshold key T exactly;
+//   4. an ordered ballot scan emits every key above T and the first kk copies of T.
+__device__ void wave_select_emit(const uint32_t* __restrict__ keys, int nv, int topk, int lo,
+                                 int32_t* __restrict__ out_idx, float* __restrict__ out_sc, uint32_t* hist,
+                                 uint32_t* list) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll 4
+  for (int j = lane; j < nv; j += 64) {
+    const uint32_t k = keys[j];
+    kmin = min(kmin, k);
+    kmax = max(kmax, k);
+  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  uint32_t kk = static_cast<uint32_t>(topk);
+  uint32_t T;
+  if (kmin == kmax) {
+    T = kmin;
   } else {
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      if (heavy[e]) score_mfma_64x128(q_I, w, k_cmp, i0 + e, lo[e], nv[e], keys[e]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    if (!heavy[e]) continue;
-    const int i = i0 + e;
-    int32_t* out_idx = idx + static_cast<long long>(i) * topk;
-    float* out_sc = score ? score + static_cast<long long>(i) * topk : nullptr;
-    if (nv[e] <= topk) {
-      for (int k = tid; k < topk; k += kThreads) {
-        out_idx[k] = (k < nv[e]) ? lo[e] + k : -1;
-        out_sc[k] = (k < nv[e]) ? order_key_to_float(keys[e][k]) : -__builtin_huge_valf();
+    const float fmin = order_key_to_float(kmin);
+    const float range = order_key_to_float(kmax) - fmin;
+    if (range > 0.f && range < __builtin_huge_valf()) {  // false for NaN keys and overflow
+      const float scale = 256.f / range;
+      wave_hist_zero(hist);
+#pragma unroll 4
+      for (int j = lane; j < nv; j += 64) atomicAdd(&hist[linear_bin(keys[j], fmin, scale)], 1u);
+      uint32_t bsel, ab;
+      wave_hist_find(hist, kk, bsel, ab);
+      kk -= ab;
+      const int m = __builtin_amdgcn_readfirstlane(static_cast<int>(hist[bsel]));
+      if (m <= kList) {
+        // compact the bin's keys (any order) and narrow the radix to their differing bits
+        uint32_t base = 0, bmin = 0xffffffffu, bmax = 0u;
+#pragma unroll 4
+        for (int j0 = 0; j0 < nv; j0 += 64) {
+          const int j = j0 + lane;
+          const uint32_t k = (j < nv) ? keys[j] : 0u;
+          const bool in = j < nv && linear_bin(k, fmin, scale) == bsel;
+          const uint64_t mk = __ballot(in);
+          const uint32_t at = base + static_cast<uint32_t>(__popcll(mk & below));
+          if (in && at < static_cast<uint32_t>(kList)) {  // at < m <= kList: the same bins as counted
+            list[at] = k;
+            bmin = min(bmin, k);
+            bmax = max(bmax, k);
+          }
+          base += static_cast<uint32_t>(__popcll(mk));
+        }
+        bmin = wave_min_u32(bmin);
+        bmax = wave_max_u32(bmax);
+        if (bmin == bmax) {
+          T = bmin;
+        } else {
+          const int top = 31 - __builtin_clz(bmin ^ bmax);
+          T = wave_radix_kth<true>(keys, nv, list, m, top, bmin, kk, -1, 0.f, 0.f, hist);
+        }
+      } else {
+        T = wave_radix_kth<false>(keys, nv, list, 0, 31, 0u, kk, static_cast<int>(bsel), fmin, scale, hist);
       }
     } else {
-      select_and_emit(keys[e], nv[e], topk, lo[e], out_idx, out_sc, sh);
+      const int top = 31 - __builtin_clz(kmin ^ kmax);
+      T = wave_radix_kth<false>(keys, nv, list, 0, top, kmin, kk, -1, 0.f, 0.f, hist);
     }
-    __syncthreads();  // the selection state is reused by the second query
+  }
+  // T is the topk-th largest key; kk of its copies are kept
+  uint32_t base_sel = 0, base_tie = 0;
+#pragma unroll 4
+  for (int j0 = 0; j0 < nv; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t key = (j < nv) ? keys[j] : 0u;
+    const bool gt = j < nv && key > T;
+    const bool eq = j < nv && key == T;
+    const uint64_t me = __ballot(eq);
+    const bool take = gt || (eq && base_tie + static_cast<uint32_t>(__popcll(me & below)) < kk);
+    const uint64_t mt = __ballot(take);
+    const uint32_t pos = base_sel + static_cast<uint32_t>(__popcll(mt & below));
+    if (take && pos < static_cast<uint32_t>(topk)) {
+      out_idx[pos] = lo + j;
+      if (out_sc) out_sc[pos] = order_key_to_float(key);
+    }
+    base_sel += static_cast<uint32_t>(__popcll(mt));
+    base_tie += static_cast<uint32_t>(__popcll(me));
+  }
+  for (int k = static_cast<int>(base_sel) + lane; k < topk; k += 64) {
+    out_idx[k] = -1;
+    if (out_sc) out_sc[k] = -__builtin_huge_valf();
   }
 }
 
-template <int PATH, typename T>
+// One wavefront per query (4 per workgroup): the row of every query: poisoned, the
+// ascending list (with scores from the keys when asked), or the top-k of the keys the
+// scoring kernel wrote.
+__global__ __launch_bounds__(kThreads) void indexer_select_kernel(
+    int Tq, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
+    const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk,
+    const uint32_t* __restrict__ keys, int32_t* __restrict__ idx, float* __restrict__ score) {
+  __shared__ uint32_t hist[kWaves][256];
+  __shared__ uint32_t list[kWaves][kList];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int i = static_cast<int>(blockIdx.x) * kWaves + wave;
+  if (i >= Tq) return;
+  int lo, nv;
+  candidate_range(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap, Tc, lo, nv);
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  nv = __builtin_amdgcn_readfirstlane(nv);
+  int32_t* out_idx = idx + static_cast<long long>(i) * topk;
+  float* out_sc = score ? score + static_cast<long long>(i) * topk : nullptr;
+  const uint32_t* my_keys = keys + static_cast<long long>(i) * cap;
+  if (nv < 0) {
+    for (int k = lane; k < topk; k += 64) {
+      out_idx[k] = -1;
+      if (out_sc) out_sc[k] = __builtin_nanf("");
+    }
+    return;
+  }
+  if (nv <= topk) {
+    for (int k = lane; k < topk; k += 64) {
+      out_idx[k] = (k < nv) ? lo + k : -1;
+      if (out_sc) out_sc[k] = (k < nv) ? order_key_to_float(my_keys[k]) : -__builtin_huge_valf();
+    }
+    return;
+  }
+  wave_select_emit(my_keys, nv, topk, lo, out_idx, out_sc, hist[wave], list[wave]);
+}
+
+// ---- pieces of indexer_score_kernel (plain functions: a by-reference lambda closure
+// would escape through the barriers' memory clobbers and put its captures in scratch)
+
+// Stage chunk c of a group's key rows into LDS buffer at lds_buf: wavefront w stages rows
+// 8 w .. 8 w + 7 (two 1 KiB instructions of 4 rows); rows past the group's nvmax
+// candidates re-read its first row.
+__device__ __forceinline__ void score_stage(const uint16_t* __restrict__ k_cmp, int glo, int nvmax, int c,
+                                            uint32_t lds_buf, int wave, int lane) {
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int rr = 8 * wave + 4 * v + (lane >> 4);
+    int cand = kChunk * c + rr;
+    cand = (cand < nvmax) ? cand : 0;
+    const uint16_t* src = k_cmp + static_cast<long long>(glo + cand) * 128 + kchunk(rr, lane & 15) * 8;
+    gather16_to_lds(src, lds_buf + static_cast<uint32_t>((8 * wave + 4 * v) * 256));
+  }
+}
+
+// B operand of block jb (candidates 16 jb + n of the staged chunk), K slots 32 ks + 8 g ..
+__device__ __forceinline__ void score_read_kf(const unsigned char* kb, int jb, int n, int g, bf16x8 (&dst)[4]) {
+  const int row = 16 * jb + n;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) dst[ks] = *reinterpret_cast<const bf16x8*>(kb + row * 256 + kchunk(row, 4 * ks + g) * 16);
+}
+
+// S[16 mb + 4 g + j, n] for the 64 heads and the block's 16 candidates
+__device__ __forceinline__ void score_block_mfma(const bf16x8 (&qa)[4][4], const bf16x8 (&kv)[4], f32x4 (&a)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      a[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[mb][ks], kv[ks], ks ? a[mb] : f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                       0);
+}
+
+// Order key of sum_h w_h * max(S_h, 0) for candidate n (every lane group gets it).  The
+// ReLU is an integer max on the bits (negative floats, -0 included, are negative
+// integers): one op, the same values as fmaxf(x, 0).
+__device__ __forceinline__ uint32_t score_block_key(const float (&wv)[4][4], const f32x4 (&a)[4]) {
+  float sc = 0.f;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc = fmaf(wv[mb][j], __int_as_float(max(__float_as_int(a[mb][j]), 0)), sc);
+  return float_order_key(quad_sum(sc));
+}
+
+// One pipeline step is one scheduling region: the next block's LDS reads first, then each
+// MFMA followed by a few VALU ops of the previous block's epilogue.
+__device__ __forceinline__ void score_interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Keys of the candidates of up to 8 consecutive local queries [8 t, 8 t + 8) (tile t), one
+// per wavefront: every query with more candidates than topk (or any candidate, when scores
+// are returned) gets the key of each candidate c < nv in keys[i * cap + c]; the queries of
+// one segment share each staged chunk of key rows.  Tiles run on XCDs in runs of kRun, so
+// a run's queries (the same segment, mostly) also share the key rows in one L2.
+__global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
+    const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp, int Tq,
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
+    const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk, int score_all,
+    int ntile, uint32_t* __restrict__ keys) {
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[kStages][kChunk * 256];
+  __shared__ int wseg[kSWaves], wlo[kSWaves], wnv[kSWaves];
+  const int xcd = static_cast<int>(blockIdx.x) & 7, kk = static_cast<int>(blockIdx.x) >> 3;
+  const int tile = ((kk / kRun) * 8 + xcd) * kRun + (kk % kRun);
+  if (tile >= ntile) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int i = 8 * tile + wave;
+  if (lane == 0) {
+    int seg = -1, lo = 0, nv = 0;
+    if (i < Tq) {
+      const int b = candidate_range(i, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap, Tc, lo, nv);
+      if (nv > topk || (score_all && nv > 0)) seg = b;
+    }
+    wseg[wave] = seg;
+    wlo[wave] = lo;
+    wnv[wave] = nv;
+  }
+  __syncthreads();
+  const bool heavy = wseg[wave] >= 0;
+  const int my_nv = __builtin_amdgcn_readfirstlane(wnv[wave]);
+  uint32_t* my_keys = keys + static_cast<long long>(i) * cap;
+  const uint32_t kbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(kst)));
+
+  // ---- phase 1: scores
+  {
+    // A operand: q_I[i, 16 mb + n, 32 ks + 8 g + 0..7]; head weights of the C rows this lane
+    // holds (heads 16 mb + 4 g + j)
+    bf16x8 qa[4][4];
+    float wv[4][4];
+    if (heavy) {
+      const uint16_t* qrow = q_I + static_cast<long long>(i) * 64 * 128;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          qa[mb][ks] = *reinterpret_cast<const bf16x8*>(qrow + (16 * mb + n) * 128 + 32 * ks + 8 * g);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wv[mb][j] = bf16_bits_to_f32(w[static_cast<long long>(i) * 64 + 16 * mb + 4 * g + j]);
+    }
+    // q_I and w are in registers before any chunk load is counted against vmcnt
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // The heavy queries of one segment form a group that shares every staged chunk; a
+    // tile straddling a segment boundary runs its groups one after the other.
+    int done = 0;
+    while (true) {
+      int gseg = -1, glo = 0, nvmax = 0, mask = 0;
+#pragma unroll
+      for (int k = 0; k < kSWaves; ++k) {
+        const int sk = wseg[k];
+        if (sk < 0 || ((done >> k) & 1)) continue;
+        if (gseg < 0) {
+          gseg = sk;
+          glo = wlo[k];
+        }
+        if (sk == gseg) {
+          mask |= 1 << k;
+          nvmax = max(nvmax, wnv[k]);
+        }
+      }
+      if (gseg < 0) break;
+      done |= mask;
+      const bool mine = (mask >> wave) & 1;
+      const int nch = (nvmax + kChunk - 1) / kChunk;
+      score_stage(k_cmp, glo, nvmax, 0, kbase, wave, lane);
+      if (nch > 1) score_stage(k_cmp, glo, nvmax, 1, kbase + kChunk * 256, wave, lane);
+      // Software pipeline over 16-candidate blocks: block (c, jb) issues its 16 MFMAs into
+      // acc0 / acc1 (alternately) while the VALU epilogue (ReLU, head weights, lane-group sum) of the
+      // previous block runs on the other buffer, so the matrix core and the VALU overlap
+      // within one wavefront; the K fragments are read one block ahead.  A live chunk
+      // computes all four blocks (the queries of one group differ by at most a few
+      // candidates, so only the last chunk's tail is wasted) to keep each step one basic
+      // block; only keys of candidates below nv are stored.
+      f32x4 acc0[4], acc1[4];
+      bf16x8 kf0[4], kf1[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      uint32_t kp0 = 0u, kp1 = 0u, kp2 = 0u;  // keys of blocks 0..2 of the previous chunk
+      uint32_t k3 = 0u;                       // key of block 3 of the previous chunk
+      for (int c = 0; c < nch; ++c) {
+        const int bf = c % kStages;
+        // chunk c has landed: the only younger vector-memory loads are chunk c + 1's two
+        // (loads retire in order; key stores in between do not matter)
+        if (c + 1 < nch) {
+          __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+        } else {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        }
+        // every wavefront's rows of chunk c are visible; every wavefront is done with
+        // chunk c - 1, whose buffer chunk c + 2 refills
+        tile_barrier();
+        if (c + 2 < nch) score_stage(k_cmp, glo, nvmax, c + 2, kbase + ((c + 2) % kStages) * kChunk * 256, wave, lane);
+        if (mine && my_nv > kChunk * c) {
+          const unsigned char* kb = kst[bf];
+          score_read_kf(kb, 0, n, g, kf0);
+          __builtin_amdgcn_sched_barrier(0);
+          score_read_kf(kb, 1, n, g, kf1);
+          score_block_mfma(qa, kf0, acc0);
+          k3 = score_block_key(wv, acc1);  // block (c - 1, 3); unused when c == 0
+          score_interleave();
+          score_read_kf(kb, 2, n, g, kf0);
+          score_block_mfma(qa, kf1, acc1);
+          const uint32_t kc0 = score_block_key(wv, acc0);
+          score_interleave();
+          score_read_kf(kb, 3, n, g, kf1);
+          score_block_mfma(qa, kf0, acc0);
+          const uint32_t kc1 = score_block_key(wv, acc1);
+          score_interleave();
+          score_block_mfma(qa, kf1, acc1);
+          const uint32_t kc2 = score_block_key(wv, acc0);
+          score_interleave();
+          if (c > 0) {
+            // lane (n, g) writes the key of candidate 64 (c - 1) + 16 g + n: one 256-byte
+            // store per chunk (selects, not an indexed array, which would live in scratch)
+            uint32_t v = kp0;
+            v = (g == 1) ? kp1 : v;
+            v = (g == 2) ? kp2 : v;
+            v = (g == 3) ? k3 : v;
+            const int cand = kChunk * (c - 1) + 16 * g + n;
+            if (cand < my_nv) my_keys[cand] = v;
+          }
+          kp0 = kc0;
+          kp1 = kc1;
+          kp2 = kc2;
+        }
+      }
+      if (mine && my_nv > 0) {
+        k3 = score_block_key(wv, acc1);
+        uint32_t v = kp0;
+        v = (g == 1) ? kp1 : v;
+        v = (g == 2) ? kp2 : v;
+        v = (g == 3) ? k3 : v;
+        const int cand = kChunk * ((my_nv - 1) / kChunk) + 16 * g + n;
+        if (cand < my_nv) my_keys[cand] = v;
+      }
+      __syncthreads();  // every wavefront is done with the buffers before the next group stages
+    }
+  }
+
+}
+
+// Small shapes: score with scalar fp32 into LDS, then select with the whole workgroup.
+template <typename T>
 __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(const T* __restrict__ q_I, const T* __restrict__ w,
                                                                 const T* __restrict__ k_cmp, int H_I, int d_I,
                                                                 const int32_t* __restrict__ cu_q,
@@ -355,11 +648,7 @@ __global__ __launch_bounds__(kThreads) void indexer_topk_kernel(const T* __restr
     return;
   }
   uint32_t* keys = dyn;
-  if constexpr (PATH == 1) {
-    score_mfma_64x128(q_I, w, k_cmp, i, lo, nv, keys);
-  } else {
-    score_generic<T>(q_I, w, k_cmp, i, H_I, d_I, lo, nv, keys, reinterpret_cast<float*>(dyn + cap));
-  }
+  score_generic<T>(q_I, w, k_cmp, i, H_I, d_I, lo, nv, keys, reinterpret_cast<float*>(dyn + cap));
   __syncthreads();
   if (nv <= topk) {
     for (int k = tid; k < topk; k += kThreads) {
@@ -378,50 +667,41 @@ bool indexer_shape_supported(int H_I, int d_I, int dtype) {
   return H_I * d_I <= 8192 && d_I % 8 == 0;
 }
 
+size_t indexer_workspace_bytes(int Tq, int cap) { return static_cast<size_t>(Tq) * static_cast<size_t>(cap) * 4; }
+
 hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp, int Tq, int Tc, int H_I, int d_I,
                                int dtype, const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_cmp,
                                const int32_t* residual, int B, int global_start, int r, int cap, int topk,
-                               int32_t* idx, float* score, hipStream_t s) {
+                               int32_t* idx, float* score, void* workspace, hipStream_t s) {
   if (Tq <= 0) return hipSuccess;
   const bool mfma = (dtype == 1 && H_I == 64 && d_I == 128);
   size_t lds = static_cast<size_t>(cap) * 4;
-  if (!mfma) lds += static_cast<size_t>(H_I) * d_I * 4 + static_cast<size_t>(H_I) * 4;
   const dim3 grid(Tq), block(kThreads);
-  // Two queries per workgroup for long candidate lists, where halving the key bytes per
-  // MFMA pays for the lower occupancy and the back-to-back selections (measured: the
-  // 22999-token CP share 2.63 -> 2.31 ms; with lists of about 1000 candidates, as in the
-  // 16k pack, one query per workgroup is faster), and only while the two key arrays
-  // leave room for two workgroups per CU.
-  const bool pair = cap >= 2048 && 2 * static_cast<size_t>(cap) * 4 <= 64 * 1024;
-  if (mfma && !pair) {
-    auto k = indexer_topk_kernel<1, uint16_t>;
-    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
-      return e;
+  if (mfma) {
+    const int ntile = (Tq + kSWaves - 1) / kSWaves;
+    const int runs = (ntile + 8 * kRun - 1) / (8 * kRun);
+    uint32_t* keys = static_cast<uint32_t*>(workspace);
+    hipLaunchKernelGGL(indexer_score_kernel, dim3(static_cast<unsigned>(runs * 8 * kRun)), dim3(kSThreads), 0, s,
+                       static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
+                       static_cast<const uint16_t*>(k_cmp), Tq, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
+                       cap, Tc, topk, score != nullptr ? 1 : 0, ntile, keys);
+    hipLaunchKernelGGL(indexer_select_kernel, dim3((Tq + kWaves - 1) / kWaves), block, 0, s, Tq, cu_q, cu_kv, cu_cmp,
+                       residual, B, global_start, r, cap, Tc, topk, keys, idx, score);
+    return hipGetLastError();
+  }
+  lds += static_cast<size_t>(H_I) * d_I * 4 + static_cast<size_t>(H_I) * 4;
+  if (dtype == 1) {
+    auto k = indexer_topk_kernel<uint16_t>;
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
-                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
-                       cap, Tc, topk, idx, score);
-  } else if (mfma) {
-    auto k = indexer_topk_pair_kernel;
-    const size_t lds2 = 2 * static_cast<size_t>(cap) * 4;
-    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds2); e != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(k, dim3((Tq + 1) / 2), block, lds2, s, static_cast<const uint16_t*>(q_I),
-                       static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(k_cmp), cu_q, cu_kv, cu_cmp, residual, B,
-                       global_start, r, cap, Tc, topk, Tq, idx, score);
-  } else if (dtype == 1) {
-    auto k = indexer_topk_kernel<0, uint16_t>;
-    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
-      return e;
-    hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
-                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
-                       cap, Tc, topk, idx, score);
+                       static_cast<const uint16_t*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start,
+                       r, cap, Tc, topk, idx, score);
   } else {
-    auto k = indexer_topk_kernel<0, float>;
-    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess)
-      return e;
+    auto k = indexer_topk_kernel<float>;
+    if (const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void*>(k), lds); e != hipSuccess) return e;
     hipLaunchKernelGGL(k, grid, block, lds, s, static_cast<const float*>(q_I), static_cast<const float*>(w),
-                       static_cast<const float*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r, cap,
-                       Tc, topk, idx, score);
+                       static_cast<const float*>(k_cmp), H_I, d_I, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
+                       cap, Tc, topk, idx, score);
   }
   return hipGetLastError();
 }

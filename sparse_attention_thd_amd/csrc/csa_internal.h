@@ -20,10 +20,12 @@ hipError_t launch_build_indices(const int32_t* cu_q, const int32_t* cu_kv, int B
 hipError_t launch_compress(const void* x, int Tkv, int d, int dtype, const int32_t* cu_kv,
                            const int32_t* cu_cmp, int B, int r, void* x_cmp, int Tc_cap, hipStream_t s);
 
+// Caller workspace of the indexer: one row of `cap` uint32 score keys per query.
+size_t indexer_workspace_bytes(int Tq, int cap);
 hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp, int Tq, int Tc, int H_I, int d_I,
                                int dtype, const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_cmp,
                                const int32_t* residual, int B, int global_start, int r, int cap, int topk,
-                               int32_t* idx, float* score, hipStream_t s);
+                               int32_t* idx, float* score, void* workspace, hipStream_t s);
 
 // `topk_rows`: cmp_idx holds csa_indexer_topk's rows for this layout (CSA_IDX_TOPK).
 hipError_t launch_sparse_mla(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,

@@ -32,18 +32,6 @@ constexpr int kKlRows = 32;      // selected rows per step of the query kernel
 constexpr int kKlTile = 128;     // compressed rows per d_k tile
 constexpr int kKlChunk = 128;    // queries per d_k chunk
 
-// K stage rows (256 bytes = 16 chunks of 16 B): chunk c of row r lives at chunk c ^ (r % 16).
-__device__ __forceinline__ int kchunk(int r, int c) { return c ^ (r & 15); }
-
-__device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_off) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
-      :
-      : "s"(lds_off), "v"(src)
-      : "memory", "m0");
-}
 
 struct KlWorkspace {
   float* G;       // [Tq][topk] loss-scaled gradient of each selected slot's score

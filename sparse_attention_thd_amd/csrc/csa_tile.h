@@ -101,6 +101,24 @@ __device__ __forceinline__ void row_to_lds(const void* row_base, uint32_t lane_o
       : "memory", "m0");
 }
 
+// Staged 256-byte rows (16 chunks of 16 B, e.g. 128 bf16 indexer keys): chunk c of row r
+// lives at chunk c ^ (r % 16), so 16 consecutive rows read at one logical chunk hit 16
+// distinct bank groups.
+__device__ __forceinline__ int kchunk(int r, int c) { return c ^ (r & 15); }
+
+// 16 bytes per lane from a per-lane global address into LDS at M0 = lds_off + 16 lane
+// (one global_load_lds_dwordx4: 1 KiB, four 256-byte rows when lanes 16 k .. 16 k + 15
+// fill row k).  Inline asm, waited on with s_waitcnt vmcnt, as row_to_lds.
+__device__ __forceinline__ void gather16_to_lds(const void* src, uint32_t lds_off) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(lds_off), "v"(src)
+      : "memory", "m0");
+}
+
 // Workgroup barrier without the full memory-counter drain that __syncthreads()
 // implies, so the next tile's global->LDS loads stay in flight across it.  The
 // empty asm keeps the compiler from moving LDS accesses across the barrier; the

@@ -102,7 +102,7 @@ def test_compress_learned_accepts_empty_streams():
 
 def _idx(**kw):
     a = dict(q=FAKE, w=FAKE, k=FAKE, Tq=8, Tc=2, H_I=64, d_I=128, dtype=1, cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE,
-             res=None, B=1, gs=0, r=4, maxlen=8, topk=512, idx=FAKE, sc=None, stream=None)
+             res=None, B=1, gs=0, r=4, maxlen=8, topk=512, idx=FAKE, sc=None, ws=FAKE, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return LIB.csa_indexer_topk(*a.values())
 
@@ -110,11 +110,20 @@ def _idx(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), EINVAL), (dict(idx=None), EINVAL), (dict(topk=0), EINVAL), (dict(B=0), EINVAL),
     (dict(maxlen=-1), EINVAL), (dict(dtype=3), EINVAL), (dict(Tc=-1), EINVAL), (dict(k=None), EINVAL),
-    (dict(topk=4096), EUNSUP),
+    (dict(ws=None), EINVAL), (dict(ws_bytes=8 * 2 * 4 - 1), EINVAL), (dict(topk=4096), EUNSUP),
     (dict(maxlen=4 * 40000), EUNSUP), (dict(H_I=128, d_I=128), EUNSUP), (dict(H_I=2, d_I=12, dtype=0), EUNSUP),
 ])
 def test_indexer_rejects(kw, code):
     assert _idx(**kw) == code
+
+
+def test_indexer_workspace_size_formula():
+    # one row of floor(max_seqlen_kv / r) uint32 score keys per query
+    assert LIB.csa_indexer_topk_workspace_bytes(10, 4039, 4) == 10 * 1009 * 4
+    assert LIB.csa_indexer_topk_workspace_bytes(32768, 22999, 4) == 32768 * 5749 * 4
+    assert LIB.csa_indexer_topk_workspace_bytes(5, 3, 4) == 0
+    assert LIB.csa_indexer_topk_workspace_bytes(-1, 8, 4) == -1
+    assert LIB.csa_indexer_topk_workspace_bytes(1, 8, 0) == -1
 
 
 def _mla(**kw):

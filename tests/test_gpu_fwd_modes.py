@@ -113,7 +113,7 @@ def test_residual_argument_matches_or_poisons_its_segment():
     for residual, expect_bad in ((res_ok, False), (res_bad, True)):
         s.csa_indexer_topk(to_device(pack.q_I), to_device(pack.w), plan.k_I_cmp, L.Tq, plan.Tc_cap, plan.H_I,
                            plan.d_I, L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, residual, L.B,
-                           L.global_start, plan.r, L.max_seqlen_kv, plan.topk, idx)
+                           L.global_start, plan.r, L.max_seqlen_kv, plan.topk, idx, workspace=plan.indexer_ws)
         torch.cuda.synchronize()
         assert torch.equal(idx[~inside], plan.topk_idx[~inside])
         if expect_bad:

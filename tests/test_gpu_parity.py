@@ -327,8 +327,12 @@ def test_binding_refuses_short_tensors():
     w = torch.zeros((Tq, 64), dtype=bf, device="cuda")
     kI = torch.zeros((16, 128), dtype=bf, device="cuda")
     idx = torch.zeros((Tq, 8), dtype=i32, device="cuda")
+    ws = torch.empty(s.csa_indexer_topk_workspace_bytes(Tq, 64, 4), dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError, match="topk_idx holds"):
-        s.csa_indexer_topk(qI, w, kI, Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 16, idx)
+        s.csa_indexer_topk(qI, w, kI, Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 16, idx, workspace=ws)
     with pytest.raises(ValueError, match="k_I_cmp holds"):
-        s.csa_indexer_topk(qI, w, kI[:15], Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 8, idx)
+        s.csa_indexer_topk(qI, w, kI[:15], Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 8, idx, workspace=ws)
+    with pytest.raises(s.CsaError, match="workspace"):  # a workspace one byte short: refused on the host
+        s.csa_indexer_topk(qI, w, kI, Tq, 16, 64, 128, cu, cu, cu_cmp, None, 1, 0, 4, 64, 8, idx,
+                           workspace=ws[:-1])
     torch.cuda.synchronize()
