@@ -183,6 +183,8 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
         slots = max(1, L.max_seqlen_kv // plan.r) if plan.cmp_kv is not None else 0
     nbytes = _lib.csa_sparse_mla_bwd_workspace_bytes(L.Tq, plan.wl, plan.wr, plan.cmp_kv, cmp_idx, topk,
                                                      L.max_seqlen_kv, plan.r)
+    torch.cuda.synchronize()
+    base_alloc = torch.cuda.memory_allocated()
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     dq = torch.empty_like(plan.out)
     d_ori = torch.empty((L.Tkv, plan.d), dtype=torch.float32, device="cuda")
@@ -197,6 +199,9 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
                                 plan.r, plan.wl, plan.wr, L.max_seqlen_kv, inputs["sinks"], plan.scale, plan.out, lse,
                                 dout, dq, d_ori, d_cmp, d_sinks, ori_l1, cmp_l1, slots, ws)
 
+    torch.cuda.synchronize()
+    call_alloc = torch.cuda.memory_allocated() - base_alloc  # workspace + every output of the call
+    torch.cuda.reset_peak_memory_stats()
     for _ in range(warmup):
         bwd()
     torch.cuda.synchronize()
@@ -206,10 +211,15 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flops = 10.0 * pack.H * pack.d * (nwin + ncmp)
+    # The library allocates nothing here: the call's memory is the caller's workspace and
+    # outputs; the peak is everything torch holds on the device while the calls run
+    # (inputs, forward outputs, workspace, gradients).
     return {"call": "csa_sparse_mla_bwd (dq, d_ori_kv, d_cmp_kv, d_sinks, ori/cmp softmax_l1_norm)",
             "steps": steps, "avg_call_ms": ms, "tokens_per_s": pack.Tq / (ms / 1e3),
             "algorithmic_flops_per_call": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12,
-            "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes}
+            "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes,
+            "workspace_bytes_per_token": nbytes / max(pack.Tq, 1), "call_buffers_bytes": call_alloc,
+            "peak_device_bytes": torch.cuda.max_memory_allocated()}
 
 
 def kl_bench(plan, pack, inputs, ncmp, steps, warmup):
@@ -341,7 +351,7 @@ def time_forward(plan, inputs, steps, warmup):
             "step": np.array([a.elapsed_time(d) for a, _, _, d in ev]), "wall": wall}
 
 
-def workload_bench(name, seed, steps, warmup):
+def workload_bench(name, seed, steps, warmup, backward=True):
     """Throughput of the whole forward on another workload's layout, inputs drawn on the
     device (same scales as the synthetic packs; the work counts depend only on the
     layout).  The sparse MLA is reported against the bf16 MFMA peak and, by its
@@ -386,6 +396,10 @@ def workload_bench(name, seed, steps, warmup):
         idx_flops = 2.0 * lay.H_I * lay.d_I * need
         res["indexer"] = {"needed_score_flops": idx_flops,
                           "frac_of_bf16_peak": idx_flops / (idx_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS}
+    if backward:
+        class PB:  # the fields backward_bench reads
+            H, d, Tq = lay.H, lay.d, lay.Tq
+        res["backward"] = backward_bench(plan, PB, inputs, nwin, ncmp, max(2, steps // 4), 1)
     del inputs, plan
     torch.cuda.empty_cache()
     return res
@@ -495,7 +509,8 @@ def main():
         result["workloads"] = {}
         for name in ("single4k", "hca32k", "cp32k"):
             if name != args.workload:
-                result["workloads"][name] = workload_bench(name, args.seed, args.steps, args.warmup)
+                result["workloads"][name] = workload_bench(name, args.seed, args.steps, args.warmup,
+                                                           backward=not args.no_backward)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(pack, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -13,7 +13,8 @@
 // candidates as N (conflict-free 16-byte LDS reads), ReLU and head weights on the fp32 C
 // fragments, a 4-lane-group sum; the keys go to the caller's workspace (one row of
 // floor(max_seqlen_kv / r) per query).  indexer_select_kernel then gives each query one
-// wavefront that selects from its keys with no workgroup barrier (wave_select_emit).
+// wavefront that selects from its keys with no workgroup barrier (wave_select_emit), the
+// keys held in registers when every list fits 6144 of them.
 // Small shapes (H_I * d_I <= 8192, either dtype): indexer_topk_kernel scores with scalar
 // fp32 straight into LDS and selects with the whole workgroup.
 #include "csa_common.h"
@@ -272,9 +273,27 @@ __device__ uint32_t wave_radix_kth(const uint32_t* __restrict__ keys, int nv, co
   return prefix;
 }
 
+// Keys of one query, slot t of lane l = key 64 t + l: KPL > 0 holds the nv <= 64 KPL keys
+// in registers (loaded once); KPL == 0 streams them from the workspace row on every pass.
+template <int KPL>
+struct WaveKeys {
+  uint32_t kr[KPL > 0 ? KPL : 1];
+  const uint32_t* __restrict__ keys;
+  int nv;
+  __device__ __forceinline__ int slots() const { return KPL > 0 ? KPL : (nv + 63) / 64; }
+  // key of slot t (0 past nv); only slots with 64 t < nv are asked for
+  __device__ __forceinline__ uint32_t at(int t, int lane) const {
+    const int j = 64 * t + lane;
+    if constexpr (KPL > 0) {
+      return kr[t];
+    } else {
+      return (j < nv) ? keys[j] : 0u;
+    }
+  }
+};
+
 // Select the topk largest of one query's nv > topk keys and write them ascending, exact
-// ties to the lower row, with this wavefront alone (no workgroup barrier), streaming the
-// keys (L2-resident after the first pass):
+// ties to the lower row, with this wavefront alone (no workgroup barrier):
 //   1. min and max key;
 //   2. a 256-bin histogram linear in the score between them (scores cluster in a few
 //      binades, so bins of the raw key bits would collide on every LDS atomic): the bin of
@@ -282,17 +301,22 @@ __device__ uint32_t wave_radix_kth(const uint32_t* __restrict__ keys, int nv, co
 //   3. the keys of that bin go to an LDS list (when they fit), and a radix select from
 //      their first differing bit finds the threshold key T exactly;
 //   4. an ordered ballot scan emits every key above T and the first kk copies of T.
-__device__ void wave_select_emit(const uint32_t* __restrict__ keys, int nv, int topk, int lo,
-                                 int32_t* __restrict__ out_idx, float* __restrict__ out_sc, uint32_t* hist,
-                                 uint32_t* list) {
+// KPL > 0: the keys sit in registers for every pass; KPL == 0: each pass streams them.
+template <int KPL>
+__device__ __forceinline__ void wave_select_emit(const WaveKeys<KPL>& K, int topk, int lo, int32_t* __restrict__ out_idx,
+                                 float* __restrict__ out_sc, uint32_t* hist, uint32_t* list) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
+  const int nv = K.nv, ns = K.slots();
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-#pragma unroll 4
-  for (int j = lane; j < nv; j += 64) {
-    const uint32_t k = keys[j];
-    kmin = min(kmin, k);
-    kmax = max(kmax, k);
+#pragma unroll
+  for (int t = 0; t < (KPL > 0 ? KPL : ns); ++t) {
+    if (64 * t >= nv) break;
+    if (64 * t + lane < nv) {
+      const uint32_t k = K.at(t, lane);
+      kmin = min(kmin, k);
+      kmax = max(kmax, k);
+    }
   }
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
@@ -306,8 +330,11 @@ __device__ void wave_select_emit(const uint32_t* __restrict__ keys, int nv, int 
     if (range > 0.f && range < __builtin_huge_valf()) {  // false for NaN keys and overflow
       const float scale = 256.f / range;
       wave_hist_zero(hist);
-#pragma unroll 4
-      for (int j = lane; j < nv; j += 64) atomicAdd(&hist[linear_bin(keys[j], fmin, scale)], 1u);
+#pragma unroll
+  for (int t = 0; t < (KPL > 0 ? KPL : ns); ++t) {
+        if (64 * t >= nv) break;
+        if (64 * t + lane < nv) atomicAdd(&hist[linear_bin(K.at(t, lane), fmin, scale)], 1u);
+      }
       uint32_t bsel, ab;
       wave_hist_find(hist, kk, bsel, ab);
       kk -= ab;
@@ -315,11 +342,11 @@ __device__ void wave_select_emit(const uint32_t* __restrict__ keys, int nv, int 
       if (m <= kList) {
         // compact the bin's keys (any order) and narrow the radix to their differing bits
         uint32_t base = 0, bmin = 0xffffffffu, bmax = 0u;
-#pragma unroll 4
-        for (int j0 = 0; j0 < nv; j0 += 64) {
-          const int j = j0 + lane;
-          const uint32_t k = (j < nv) ? keys[j] : 0u;
-          const bool in = j < nv && linear_bin(k, fmin, scale) == bsel;
+#pragma unroll
+  for (int t = 0; t < (KPL > 0 ? KPL : ns); ++t) {
+          if (64 * t >= nv) break;
+          const uint32_t k = K.at(t, lane);
+          const bool in = 64 * t + lane < nv && linear_bin(k, fmin, scale) == bsel;
           const uint64_t mk = __ballot(in);
           const uint32_t at = base + static_cast<uint32_t>(__popcll(mk & below));
           if (in && at < static_cast<uint32_t>(kList)) {  // at < m <= kList: the same bins as counted
@@ -335,22 +362,23 @@ __device__ void wave_select_emit(const uint32_t* __restrict__ keys, int nv, int 
           T = bmin;
         } else {
           const int top = 31 - __builtin_clz(bmin ^ bmax);
-          T = wave_radix_kth<true>(keys, nv, list, m, top, bmin, kk, -1, 0.f, 0.f, hist);
+          T = wave_radix_kth<true>(K.keys, nv, list, m, top, bmin, kk, -1, 0.f, 0.f, hist);
         }
       } else {
-        T = wave_radix_kth<false>(keys, nv, list, 0, 31, 0u, kk, static_cast<int>(bsel), fmin, scale, hist);
+        T = wave_radix_kth<false>(K.keys, nv, list, 0, 31, 0u, kk, static_cast<int>(bsel), fmin, scale, hist);
       }
     } else {
       const int top = 31 - __builtin_clz(kmin ^ kmax);
-      T = wave_radix_kth<false>(keys, nv, list, 0, top, kmin, kk, -1, 0.f, 0.f, hist);
+      T = wave_radix_kth<false>(K.keys, nv, list, 0, top, kmin, kk, -1, 0.f, 0.f, hist);
     }
   }
   // T is the topk-th largest key; kk of its copies are kept
   uint32_t base_sel = 0, base_tie = 0;
-#pragma unroll 4
-  for (int j0 = 0; j0 < nv; j0 += 64) {
-    const int j = j0 + lane;
-    const uint32_t key = (j < nv) ? keys[j] : 0u;
+#pragma unroll
+  for (int t = 0; t < (KPL > 0 ? KPL : ns); ++t) {
+    if (64 * t >= nv) break;
+    const int j = 64 * t + lane;
+    const uint32_t key = K.at(t, lane);
     const bool gt = j < nv && key > T;
     const bool eq = j < nv && key == T;
     const uint64_t me = __ballot(eq);
@@ -372,7 +400,8 @@ __device__ void wave_select_emit(const uint32_t* __restrict__ keys, int nv, int 
 
 // One wavefront per query (4 per workgroup): the row of every query: poisoned, the
 // ascending list (with scores from the keys when asked), or the top-k of the keys the
-// scoring kernel wrote.
+// scoring kernel wrote (KPL > 0: every candidate list fits 64 KPL keys in registers).
+template <int KPL>
 __global__ __launch_bounds__(kThreads) void indexer_select_kernel(
     int Tq, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
     const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk,
@@ -404,7 +433,14 @@ __global__ __launch_bounds__(kThreads) void indexer_select_kernel(
     }
     return;
   }
-  wave_select_emit(my_keys, nv, topk, lo, out_idx, out_sc, hist[wave], list[wave]);
+  WaveKeys<KPL> K;
+  K.keys = my_keys;
+  K.nv = nv;
+  if constexpr (KPL > 0) {
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) K.kr[t] = (64 * t + lane < nv) ? my_keys[64 * t + lane] : 0u;
+  }
+  wave_select_emit<KPL>(K, topk, lo, out_idx, out_sc, hist[wave], list[wave]);
 }
 
 // ---- pieces of indexer_score_kernel (plain functions: a by-reference lambda closure
@@ -685,8 +721,24 @@ hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp
                        static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
                        static_cast<const uint16_t*>(k_cmp), Tq, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
                        cap, Tc, topk, score != nullptr ? 1 : 0, ntile, keys);
-    hipLaunchKernelGGL(indexer_select_kernel, dim3((Tq + kWaves - 1) / kWaves), block, 0, s, Tq, cu_q, cu_kv, cu_cmp,
-                       residual, B, global_start, r, cap, Tc, topk, keys, idx, score);
+    // keys in registers up to 6144 candidates per query (one read of the workspace row),
+    // streamed from the row on every pass beyond that
+    const dim3 sgrid((Tq + kWaves - 1) / kWaves);
+#define CSA_SELECT(KPL)                                                                                     \
+  hipLaunchKernelGGL(indexer_select_kernel<KPL>, sgrid, block, 0, s, Tq, cu_q, cu_kv, cu_cmp, residual, B, \
+                     global_start, r, cap, Tc, topk, keys, idx, score)
+    if (cap <= 64 * 16) {
+      CSA_SELECT(16);
+    } else if (cap <= 64 * 32) {
+      CSA_SELECT(32);
+    } else if (cap <= 64 * 64) {
+      CSA_SELECT(64);
+    } else if (cap <= 64 * 96) {
+      CSA_SELECT(96);
+    } else {
+      CSA_SELECT(0);
+    }
+#undef CSA_SELECT
     return hipGetLastError();
   }
   lds += static_cast<size_t>(H_I) * d_I * 4 + static_cast<size_t>(H_I) * 4;
