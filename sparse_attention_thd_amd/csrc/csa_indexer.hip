@@ -171,9 +171,12 @@ __device__ __forceinline__ void write_poisoned_row(int32_t* __restrict__ out_idx
   }
 }
 
-constexpr int kSThreads = 512;             // fused workgroup: 8 wavefronts, one query each
+constexpr int kSThreads = 512;             // scoring workgroup: 8 wavefronts, one query each
 constexpr int kSWaves = kSThreads / 64;
-constexpr int kChunk = 64;                 // candidates per LDS chunk (64 rows of 256 B)
+// Candidates per LDS chunk (rows of 256 B) are a template parameter CH of the scoring
+// kernel: 128 (half the barriers) for long candidate lists, 64 (half the tail of the last
+// chunk) for short ones.  CH / 16 MFMA blocks per chunk; each of the 8 wavefronts stages
+// CH / 32 rows-of-4 (1 KiB global_load_lds) per chunk.
 constexpr int kStages = 3;                 // chunk buffers: loads run two chunks ahead
 constexpr int kRun = 4;                    // consecutive tiles per XCD run
 
@@ -447,17 +450,18 @@ __global__ __launch_bounds__(kThreads) void indexer_select_kernel(
 // would escape through the barriers' memory clobbers and put its captures in scratch)
 
 // Stage chunk c of a group's key rows into LDS buffer at lds_buf: wavefront w stages rows
-// 8 w .. 8 w + 7 (two 1 KiB instructions of 4 rows); rows past the group's nvmax
-// candidates re-read its first row.
+// CH / 8 * w onward (CH / 32 1 KiB instructions of 4 rows); rows past the group's
+// nvmax candidates re-read its first row.
+template <int CH>
 __device__ __forceinline__ void score_stage(const uint16_t* __restrict__ k_cmp, int glo, int nvmax, int c,
                                             uint32_t lds_buf, int wave, int lane) {
 #pragma unroll
-  for (int v = 0; v < 2; ++v) {
-    const int rr = 8 * wave + 4 * v + (lane >> 4);
-    int cand = kChunk * c + rr;
+  for (int v = 0; v < CH / 32; ++v) {
+    const int rr = (CH / kSWaves) * wave + 4 * v + (lane >> 4);
+    int cand = CH * c + rr;
     cand = (cand < nvmax) ? cand : 0;
     const uint16_t* src = k_cmp + static_cast<long long>(glo + cand) * 128 + kchunk(rr, lane & 15) * 8;
-    gather16_to_lds(src, lds_buf + static_cast<uint32_t>((8 * wave + 4 * v) * 256));
+    gather16_to_lds(src, lds_buf + static_cast<uint32_t>(((CH / kSWaves) * wave + 4 * v) * 256));
   }
 }
 
@@ -490,6 +494,18 @@ __device__ __forceinline__ uint32_t score_block_key(const float (&wv)[4][4], con
   return float_order_key(quad_sum(sc));
 }
 
+// Lane (n, g) writes the keys of candidates base + 64 q + 16 g + n (blocks 4 q + g, which
+// this lane kept in mine[q]): one 256-byte store per four blocks.
+template <int NQ>
+__device__ __forceinline__ void score_store_keys(const uint32_t (&mine)[NQ], uint32_t* __restrict__ my_keys, int base,
+                                                 int nv, int n, int g) {
+#pragma unroll
+  for (int qd = 0; qd < NQ; ++qd) {
+    const int cand = base + 64 * qd + 16 * g + n;
+    if (cand < nv) my_keys[cand] = mine[qd];
+  }
+}
+
 // One pipeline step is one scheduling region: the next block's LDS reads first, then each
 // MFMA followed by a few VALU ops of the previous block's epilogue.
 __device__ __forceinline__ void score_interleave() {
@@ -507,13 +523,15 @@ __device__ __forceinline__ void score_interleave() {
 // are returned) gets the key of each candidate c < nv in keys[i * cap + c]; the queries of
 // one segment share each staged chunk of key rows.  Tiles run on XCDs in runs of kRun, so
 // a run's queries (the same segment, mostly) also share the key rows in one L2.
+template <int CH>
 __global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
     const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp, int Tq,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
     const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk, int score_all,
     int ntile, uint32_t* __restrict__ keys) {
-  __shared__ __attribute__((aligned(1024))) unsigned char kst[kStages][kChunk * 256];
+  __shared__ __attribute__((aligned(1024))) unsigned char kst[kStages][CH * 256];
   __shared__ int wseg[kSWaves], wlo[kSWaves], wnv[kSWaves];
+  constexpr int NB = CH / 16;
   const int xcd = static_cast<int>(blockIdx.x) & 7, kk = static_cast<int>(blockIdx.x) >> 3;
   const int tile = ((kk / kRun) * 8 + xcd) * kRun + (kk % kRun);
   if (tile >= ntile) return;
@@ -579,77 +597,65 @@ __global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
       if (gseg < 0) break;
       done |= mask;
       const bool mine = (mask >> wave) & 1;
-      const int nch = (nvmax + kChunk - 1) / kChunk;
-      score_stage(k_cmp, glo, nvmax, 0, kbase, wave, lane);
-      if (nch > 1) score_stage(k_cmp, glo, nvmax, 1, kbase + kChunk * 256, wave, lane);
+      const int nch = (nvmax + CH - 1) / CH;
+      score_stage<CH>(k_cmp, glo, nvmax, 0, kbase, wave, lane);
+      if (nch > 1) score_stage<CH>(k_cmp, glo, nvmax, 1, kbase + CH * 256, wave, lane);
       // Software pipeline over 16-candidate blocks: block (c, jb) issues its 16 MFMAs into
       // acc0 / acc1 (alternately) while the VALU epilogue (ReLU, head weights, lane-group sum) of the
       // previous block runs on the other buffer, so the matrix core and the VALU overlap
       // within one wavefront; the K fragments are read one block ahead.  A live chunk
-      // computes all four blocks (the queries of one group differ by at most a few
+      // computes every block (the queries of one group differ by at most a few
       // candidates, so only the last chunk's tail is wasted) to keep each step one basic
       // block; only keys of candidates below nv are stored.
       f32x4 acc0[4], acc1[4];
       bf16x8 kf0[4], kf1[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) acc1[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      uint32_t kp0 = 0u, kp1 = 0u, kp2 = 0u;  // keys of blocks 0..2 of the previous chunk
-      uint32_t k3 = 0u;                       // key of block 3 of the previous chunk
+      // keys of blocks 4 q + g: every lane group holds every block's key after the lane-group
+      // sum, and lane group g keeps those of blocks 4 q + g (a conditional move per block
+      // with a constant block index; a select over an indexed array would live in scratch)
+      uint32_t pm[NB / 4], cm[NB / 4];  // the previous chunk's (its last block once reduced), this chunk's
+#pragma unroll
+      for (int qd = 0; qd < NB / 4; ++qd) pm[qd] = cm[qd] = 0u;
       for (int c = 0; c < nch; ++c) {
         const int bf = c % kStages;
-        // chunk c has landed: the only younger vector-memory loads are chunk c + 1's two
+        // chunk c has landed: the only younger vector-memory loads are chunk c + 1's
         // (loads retire in order; key stores in between do not matter)
         if (c + 1 < nch) {
-          __builtin_amdgcn_s_waitcnt(0x0F72);  // vmcnt(2)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (CH / 32));  // vmcnt(CH / 32)
         } else {
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         // every wavefront's rows of chunk c are visible; every wavefront is done with
         // chunk c - 1, whose buffer chunk c + 2 refills
         tile_barrier();
-        if (c + 2 < nch) score_stage(k_cmp, glo, nvmax, c + 2, kbase + ((c + 2) % kStages) * kChunk * 256, wave, lane);
-        if (mine && my_nv > kChunk * c) {
+        if (c + 2 < nch) score_stage<CH>(k_cmp, glo, nvmax, c + 2, kbase + ((c + 2) % kStages) * CH * 256, wave, lane);
+        if (mine && my_nv > CH * c) {
           const unsigned char* kb = kst[bf];
           score_read_kf(kb, 0, n, g, kf0);
           __builtin_amdgcn_sched_barrier(0);
-          score_read_kf(kb, 1, n, g, kf1);
-          score_block_mfma(qa, kf0, acc0);
-          k3 = score_block_key(wv, acc1);  // block (c - 1, 3); unused when c == 0
-          score_interleave();
-          score_read_kf(kb, 2, n, g, kf0);
-          score_block_mfma(qa, kf1, acc1);
-          const uint32_t kc0 = score_block_key(wv, acc0);
-          score_interleave();
-          score_read_kf(kb, 3, n, g, kf1);
-          score_block_mfma(qa, kf0, acc0);
-          const uint32_t kc1 = score_block_key(wv, acc1);
-          score_interleave();
-          score_block_mfma(qa, kf1, acc1);
-          const uint32_t kc2 = score_block_key(wv, acc0);
-          score_interleave();
-          if (c > 0) {
-            // lane (n, g) writes the key of candidate 64 (c - 1) + 16 g + n: one 256-byte
-            // store per chunk (selects, not an indexed array, which would live in scratch)
-            uint32_t v = kp0;
-            v = (g == 1) ? kp1 : v;
-            v = (g == 2) ? kp2 : v;
-            v = (g == 3) ? k3 : v;
-            const int cand = kChunk * (c - 1) + 16 * g + n;
-            if (cand < my_nv) my_keys[cand] = v;
+#pragma unroll
+          for (int jb = 0; jb < NB; ++jb) {
+            if (jb + 1 < NB) score_read_kf(kb, jb + 1, n, g, ((jb + 1) & 1) ? kf1 : kf0);
+            score_block_mfma(qa, (jb & 1) ? kf1 : kf0, (jb & 1) ? acc1 : acc0);
+            if (jb == 0) {
+              const uint32_t kx = score_block_key(wv, acc1);  // block (c - 1, NB - 1); unused when c == 0
+              pm[NB / 4 - 1] = (g == 3) ? kx : pm[NB / 4 - 1];
+            } else {
+              const uint32_t kx = score_block_key(wv, ((jb - 1) & 1) ? acc1 : acc0);
+              cm[(jb - 1) / 4] = (g == (jb - 1) % 4) ? kx : cm[(jb - 1) / 4];
+            }
+            score_interleave();
           }
-          kp0 = kc0;
-          kp1 = kc1;
-          kp2 = kc2;
+          if (c > 0) score_store_keys(pm, my_keys, CH * (c - 1), my_nv, n, g);
+#pragma unroll
+          for (int qd = 0; qd < NB / 4; ++qd) pm[qd] = cm[qd];
         }
       }
       if (mine && my_nv > 0) {
-        k3 = score_block_key(wv, acc1);
-        uint32_t v = kp0;
-        v = (g == 1) ? kp1 : v;
-        v = (g == 2) ? kp2 : v;
-        v = (g == 3) ? k3 : v;
-        const int cand = kChunk * ((my_nv - 1) / kChunk) + 16 * g + n;
-        if (cand < my_nv) my_keys[cand] = v;
+        const uint32_t kx = score_block_key(wv, acc1);
+        pm[NB / 4 - 1] = (g == 3) ? kx : pm[NB / 4 - 1];
+        score_store_keys(pm, my_keys, CH * ((my_nv - 1) / CH), my_nv, n, g);
       }
       __syncthreads();  // every wavefront is done with the buffers before the next group stages
     }
@@ -717,7 +723,9 @@ hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp
     const int ntile = (Tq + kSWaves - 1) / kSWaves;
     const int runs = (ntile + 8 * kRun - 1) / (8 * kRun);
     uint32_t* keys = static_cast<uint32_t*>(workspace);
-    hipLaunchKernelGGL(indexer_score_kernel, dim3(static_cast<unsigned>(runs * 8 * kRun)), dim3(kSThreads), 0, s,
+    // long candidate lists: 128-row chunks (half the barriers); short ones: 64 (half the tail)
+    auto score_kernel = (cap >= 2048) ? indexer_score_kernel<128> : indexer_score_kernel<64>;
+    hipLaunchKernelGGL(score_kernel, dim3(static_cast<unsigned>(runs * 8 * kRun)), dim3(kSThreads), 0, s,
                        static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
                        static_cast<const uint16_t*>(k_cmp), Tq, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
                        cap, Tc, topk, score != nullptr ? 1 : 0, ntile, keys);
