@@ -157,7 +157,7 @@ def gather_phases(plan, pack, ms):
             "algorithmic_bytes": total, "achieved_GBps": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
 
 
-def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
+def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup, deterministic=False):
     """csa_sparse_mla_bwd on the forward's output and lse with a seeded bf16 dout.
 
     Algorithmic work: five products of 64 heads x 512 dims per attended (query, key)
@@ -211,6 +211,29 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     flops = 10.0 * pack.H * pack.d * (nwin + ncmp)
+    peak = torch.cuda.max_memory_allocated()  # of the atomic call, before the deterministic one
+    res_det = None
+    if deterministic:
+        # the same call with bit-reproducible row gradients (per-item tiles + an ordered reduce)
+        dbytes = _lib.csa_sparse_mla_bwd_deterministic_workspace_bytes(L.Tq, L.B, plan.wl, plan.wr, plan.cmp_kv,
+                                                                       cmp_idx, topk, L.max_seqlen_kv, plan.r)
+        dws = torch.empty(max(dbytes, 1), dtype=torch.uint8, device="cuda")
+
+        def bwd_det():
+            _lib.csa_sparse_mla_bwd_deterministic(
+                inputs["q"], inputs["ori_kv"], plan.cmp_kv, cmp_idx, topk, L.Tq, L.Tkv, Tc, plan.H, plan.d,
+                L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp, L.B, L.global_start, plan.r, plan.wl, plan.wr,
+                L.max_seqlen_kv, inputs["sinks"], plan.scale, plan.out, lse, dout, dq, d_ori, d_cmp, d_sinks, ori_l1,
+                cmp_l1, slots, dws)
+        for _ in range(warmup):
+            bwd_det()
+        torch.cuda.synchronize()
+        evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for e0, e1 in evd:
+            e0.record(); bwd_det(); e1.record()
+        torch.cuda.synchronize()
+        res_det = {"avg_call_ms": float(np.mean([a.elapsed_time(b) for a, b in evd])), "workspace_bytes": dbytes}
+        del dws
     # The library allocates nothing here: the call's memory is the caller's workspace and
     # outputs; the peak is everything torch holds on the device while the calls run
     # (inputs, forward outputs, workspace, gradients).
@@ -219,7 +242,7 @@ def backward_bench(plan, pack, inputs, nwin, ncmp, steps, warmup):
             "algorithmic_flops_per_call": flops, "achieved_tflops": flops / (ms / 1e3) / 1e12,
             "frac_of_bf16_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, "workspace_bytes": nbytes,
             "workspace_bytes_per_token": nbytes / max(pack.Tq, 1), "call_buffers_bytes": call_alloc,
-            "peak_device_bytes": torch.cuda.max_memory_allocated()}
+            "peak_device_bytes": peak, "deterministic": res_det}
 
 
 def kl_bench(plan, pack, inputs, ncmp, steps, warmup):
@@ -498,7 +521,7 @@ def main():
         "host_wall_s": wall,
     }
     if not args.no_backward and pack.H == 64 and pack.d == 512:
-        result["backward"] = backward_bench(plan, pack, inputs, nwin, ncmp, args.bwd_steps, 2)
+        result["backward"] = backward_bench(plan, pack, inputs, nwin, ncmp, args.bwd_steps, 2, deterministic=True)
     if not args.no_kl and plan.topk_idx is not None and pack.H_I == 64 and pack.d_I == 128:
         result["indexer_kl"] = kl_bench(plan, pack, inputs, ncmp, args.bwd_steps, 2)
     if not args.no_learned and plan.r == 4 and plan.Tc_cap > 0:

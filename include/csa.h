@@ -284,7 +284,8 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
  * (query, key) pair as 256-byte rows, key rows, sink terms, the selection map),
  * owned by the caller; no memory is allocated.  d_ori_kv and d_cmp_kv take float
  * atomics from the work items that share a key tile, so their last bits vary from
- * run to run; dq, d_sinks and the l1 outputs are deterministic.
+ * run to run (csa_sparse_mla_bwd_deterministic below does not); dq, d_sinks and the
+ * l1 outputs are deterministic.
  * Errors: as csa_sparse_mla_fwd, plus EINVAL for a missing out/lse/dout/dq/
  * workspace/d_ori_kv, cmp_kv without d_cmp_kv, sinks without d_sinks, cmp_l1 with
  * cmp_slots < 1, or a workspace smaller than required; EUNSUPPORTED for any shape
@@ -301,6 +302,38 @@ int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, co
                        const void* out, const float* lse, const void* dout, void* dq, float* d_ori_kv,
                        float* d_cmp_kv, float* d_sinks, float* ori_l1, float* cmp_l1, int32_t cmp_slots,
                        void* workspace, int64_t workspace_bytes, csa_stream_t stream);
+
+/*
+ * csa_sparse_mla_bwd_deterministic - csa_sparse_mla_bwd with bit-reproducible row
+ * gradients (the gradients of [HP] 4. npu_sparse_flash_mla_grad; the page's GPU
+ * verification of the unfused path reports bit-identical reruns).
+ *
+ * Same arguments, results and errors as csa_sparse_mla_bwd.  Each row-gradient work
+ * item (a key tile of up to 256 rows, 256 latent dims, swept by a chunk of up to 128
+ * queries) writes its float32 tile to its own slot of the workspace instead of adding
+ * it with atomics, and one more kernel sums, for every row of d_ori_kv and d_cmp_kv,
+ * the tiles that hold it in ascending query-chunk order and stores the row.  Every
+ * output is then identical from run to run; d_ori_kv / d_cmp_kv equal
+ * csa_sparse_mla_bwd's up to float32 summation order.  workspace: at least
+ * csa_sparse_mla_bwd_deterministic_workspace_bytes() bytes: csa_sparse_mla_bwd's
+ * workspace plus the tiles, (ceil(Tq / 128) + B) chunks x 2 (n_w + n_c) items x 256 KiB
+ * with n_w = min(127 + ori_win_left + ori_win_right, max_seqlen_kv - 1) / 256 + 1 and
+ * n_c = ceil(floor(max_seqlen_kv / cmp_ratio) / 256) (0 without cmp_kv); -1 for
+ * invalid sizes (B < 1 among them).
+ */
+int64_t csa_sparse_mla_bwd_deterministic_workspace_bytes(int32_t Tq, int32_t B, int32_t ori_win_left,
+                                                         int32_t ori_win_right, const void* cmp_kv,
+                                                         const int32_t* cmp_idx, int32_t topk,
+                                                         int32_t max_seqlen_kv, int32_t cmp_ratio);
+int csa_sparse_mla_bwd_deterministic(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
+                                     int32_t topk, int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d,
+                                     int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                     const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start,
+                                     int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
+                                     int32_t max_seqlen_kv, const float* sinks, float softmax_scale, const void* out,
+                                     const float* lse, const void* dout, void* dq, float* d_ori_kv, float* d_cmp_kv,
+                                     float* d_sinks, float* ori_l1, float* cmp_l1, int32_t cmp_slots,
+                                     void* workspace, int64_t workspace_bytes, csa_stream_t stream);
 
 /*
  * csa_indexer_kl_grad - the lightning indexer's KL loss against the main attention and

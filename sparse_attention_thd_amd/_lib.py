@@ -37,6 +37,10 @@ SIGNATURES = {
     "csa_sparse_mla_bwd_workspace_bytes": [_I, _I, _I, _P, _P, _I, _I, _I],
     "csa_sparse_mla_bwd": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
                            C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, C.c_int64, _P],
+    "csa_sparse_mla_bwd_deterministic_workspace_bytes": [_I, _I, _I, _I, _P, _P, _I, _I, _I],
+    "csa_sparse_mla_bwd_deterministic": [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, _I,
+                                         _I, _P, C.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, C.c_int64,
+                                         _P],
     "csa_indexer_kl_grad_workspace_bytes": [_I, _I, _I, _I],
     "csa_indexer_kl_grad": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I, C.c_float,
                             _P, _P, _P, _P, _P, C.c_int64, _P],
@@ -45,6 +49,7 @@ SIGNATURES = {
     "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
 }
 RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64,
+            "csa_sparse_mla_bwd_deterministic_workspace_bytes": C.c_int64,
             "csa_indexer_topk_workspace_bytes": C.c_int64,
             "csa_indexer_kl_grad_workspace_bytes": C.c_int64}
 
@@ -201,15 +206,25 @@ def csa_sparse_mla_bwd_workspace_bytes(Tq, ori_win_left, ori_win_right, cmp_kv, 
     return int(n)
 
 
-def csa_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv,
-                       cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv,
-                       sinks, softmax_scale, out, lse, dout, dq, d_ori_kv, d_cmp_kv=None, d_sinks=None,
-                       ori_l1=None, cmp_l1=None, cmp_slots=0, workspace=None, stream=None):
+def csa_sparse_mla_bwd_deterministic_workspace_bytes(Tq, B, ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk,
+                                                     max_seqlen_kv, cmp_ratio):
+    n = LIB.csa_sparse_mla_bwd_deterministic_workspace_bytes(Tq, B, ori_win_left, ori_win_right,
+                                                             _ptr(cmp_kv, "cmp_kv", optional=True),
+                                                             _ptr(cmp_idx, "cmp_idx", torch.int32, True), topk,
+                                                             max_seqlen_kv, cmp_ratio)
+    if n < 0:
+        raise CsaError(CSA_EINVAL, "csa_sparse_mla_bwd_deterministic_workspace_bytes: invalid arguments")
+    return int(n)
+
+
+def _bwd(fn, q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B,
+         global_start, cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks, softmax_scale, out, lse, dout,
+         dq, d_ori_kv, d_cmp_kv, d_sinks, ori_l1, cmp_l1, cmp_slots, workspace, stream):
     i32, f32 = torch.int32, torch.float32
     dt = q.dtype
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     nq, W = Tq * H * d, ori_win_left + ori_win_right + 1
-    _check(LIB.csa_sparse_mla_bwd(
+    _check(fn(
         _ptr(q, "q", need=nq), _ptr(ori_kv, "ori_kv", dt, need=Tkv * d), _ptr(cmp_kv, "cmp_kv", dt, True, Tc * d),
         _ptr(cmp_idx, "cmp_idx", i32, True, Tq * topk), topk, Tq, Tkv, Tc, H, d, _dtype_code(q),
         _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
@@ -220,6 +235,25 @@ def csa_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_s
         _ptr(d_cmp_kv, "d_cmp_kv", f32, True, Tc * d), _ptr(d_sinks, "d_sinks", f32, True, H),
         _ptr(ori_l1, "ori_l1", f32, True, Tq * W), _ptr(cmp_l1, "cmp_l1", f32, True, Tq * cmp_slots), cmp_slots,
         _ptr(workspace, "workspace", optional=True), ws_bytes, _stream(stream)))
+
+
+def csa_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv,
+                       cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv,
+                       sinks, softmax_scale, out, lse, dout, dq, d_ori_kv, d_cmp_kv=None, d_sinks=None,
+                       ori_l1=None, cmp_l1=None, cmp_slots=0, workspace=None, stream=None):
+    _bwd(LIB.csa_sparse_mla_bwd, q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q, cu_seqlens_kv,
+         cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks, softmax_scale,
+         out, lse, dout, dq, d_ori_kv, d_cmp_kv, d_sinks, ori_l1, cmp_l1, cmp_slots, workspace, stream)
+
+
+def csa_sparse_mla_bwd_deterministic(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q,
+                                     cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left,
+                                     ori_win_right, max_seqlen_kv, sinks, softmax_scale, out, lse, dout, dq, d_ori_kv,
+                                     d_cmp_kv=None, d_sinks=None, ori_l1=None, cmp_l1=None, cmp_slots=0,
+                                     workspace=None, stream=None):
+    _bwd(LIB.csa_sparse_mla_bwd_deterministic, q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, cu_seqlens_q,
+         cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks,
+         softmax_scale, out, lse, dout, dq, d_ori_kv, d_cmp_kv, d_sinks, ori_l1, cmp_l1, cmp_slots, workspace, stream)
 
 
 def csa_indexer_kl_grad_workspace_bytes(Tq, topk, max_seqlen_kv, cmp_ratio):

@@ -207,6 +207,71 @@ int64_t csa_sparse_mla_bwd_workspace_bytes(int32_t Tq, int32_t ori_win_left, int
                                                                                  cmp_ratio)));
 }
 
+// Partial row-gradient tiles of the deterministic backward (after the common workspace).
+static int64_t bwd_partial_bytes(int32_t Tq, int32_t B, int32_t wl, int32_t wr, int32_t Tkv, const void* cmp_kv,
+                                 int32_t max_seqlen_kv, int32_t cmp_ratio) {
+  return static_cast<int64_t>(csa::mla_bwd_partial_bytes(Tq, B, wl, wr, Tkv, cmp_kv != nullptr, max_seqlen_kv,
+                                                         cmp_ratio));
+}
+
+int64_t csa_sparse_mla_bwd_deterministic_workspace_bytes(int32_t Tq, int32_t B, int32_t ori_win_left,
+                                                         int32_t ori_win_right, const void* cmp_kv,
+                                                         const int32_t* cmp_idx, int32_t topk, int32_t max_seqlen_kv,
+                                                         int32_t cmp_ratio) {
+  const int64_t base = csa_sparse_mla_bwd_workspace_bytes(Tq, ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk,
+                                                          max_seqlen_kv, cmp_ratio);
+  if (base < 0 || B < 1) return -1;
+  return base + bwd_partial_bytes(Tq, B, ori_win_left, ori_win_right, 0x7fffffff, cmp_kv, max_seqlen_kv, cmp_ratio);
+}
+
+static int bwd_call(const char* name, bool deterministic, const void* q, const void* ori_kv, const void* cmp_kv,
+                    const int32_t* cmp_idx, int32_t topk, int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d,
+                    int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                    const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start, int32_t cmp_ratio,
+                    int32_t ori_win_left, int32_t ori_win_right, int32_t max_seqlen_kv, const float* sinks,
+                    float softmax_scale, const void* out, const float* lse, const void* dout, void* dq,
+                    float* d_ori_kv, float* d_cmp_kv, float* d_sinks, float* ori_l1, float* cmp_l1,
+                    int32_t cmp_slots, void* workspace, int64_t workspace_bytes, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv || !ori_kv || !d_ori_kv ||
+      (Tq != 0 && (!q || !out || !lse || !dout || !dq || !workspace)))
+    return fail(CSA_EINVAL, "%s: NULL pointer", name);
+  if (cmp_kv && (!cu_seqlens_cmp || !d_cmp_kv)) return fail(CSA_EINVAL, "%s: cmp_kv needs cu_seqlens_cmp and d_cmp_kv", name);
+  if (cmp_idx && !cmp_kv) return fail(CSA_EINVAL, "%s: cmp_idx given without cmp_kv", name);
+  if (cmp_idx && topk < 1) return fail(CSA_EINVAL, "%s: topk must be >= 1 with cmp_idx", name);
+  if (sinks && !d_sinks) return fail(CSA_EINVAL, "%s: sinks need d_sinks", name);
+  if (cmp_l1 && cmp_slots < 1) return fail(CSA_EINVAL, "%s: cmp_l1 needs cmp_slots >= 1", name);
+  if (B < 1 || Tq < 0 || Tkv < 0 || Tc < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0 ||
+      max_seqlen_kv < 0 || cmp_slots < 0)
+    return fail(CSA_EINVAL, "%s: invalid size or parameter", name);
+  if (!window_fits(ori_win_left, ori_win_right, Tkv))
+    return fail(CSA_EINVAL, "%s: window sides must be >= 0 with Tkv + sides < 2^31", name);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(CSA_EINVAL, "%s: softmax_scale (%g) must be positive and finite", name,
+                static_cast<double>(softmax_scale));
+  if (static_cast<long long>(global_start) + Tq > Tkv)
+    return fail(CSA_EINVAL, "%s: global_start + Tq exceeds Tkv", name);
+  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "%s: unknown dtype %d", name, dtype);
+  if (cmp_idx && topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "%s: topk %d > %d", name, topk, kMaxTopk);
+  if (!csa::mla_bwd_shape_supported(H, d, dtype))
+    return fail(CSA_EUNSUPPORTED, "%s: no kernel for H=%d d=%d dtype=%d", name, H, d, dtype);
+  const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
+  const int nvis_cap = bwd_nvis_cap(cmp_kv, cmp_idx, max_seqlen_kv, cmp_ratio);
+  int64_t need = static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap, nvis_cap));
+  if (deterministic)
+    need += bwd_partial_bytes(Tq, B, ori_win_left, ori_win_right, Tkv, cmp_kv, max_seqlen_kv, cmp_ratio);
+  if (workspace_bytes < need)
+    return fail(CSA_EINVAL, "%s: workspace of %lld bytes < %lld needed", name,
+                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+  return hip_status(csa::launch_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, cmp_kv ? Tc : 0,
+                                               cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
+                                               cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks,
+                                               softmax_scale, out, lse, dout, dq, d_ori_kv,
+                                               cmp_kv ? d_cmp_kv : nullptr, d_sinks, ori_l1, cmp_l1, cmp_slots, cap,
+                                               nvis_cap, workspace, deterministic,
+                                               static_cast<hipStream_t>(stream)),
+                    name);
+}
+
 int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
                        int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d, int32_t dtype,
                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp,
@@ -215,42 +280,25 @@ int csa_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, co
                        const void* out, const float* lse, const void* dout, void* dq, float* d_ori_kv,
                        float* d_cmp_kv, float* d_sinks, float* ori_l1, float* cmp_l1, int32_t cmp_slots,
                        void* workspace, int64_t workspace_bytes, csa_stream_t stream) {
-  if (!cu_seqlens_q || !cu_seqlens_kv || !ori_kv || !d_ori_kv ||
-      (Tq != 0 && (!q || !out || !lse || !dout || !dq || !workspace)))
-    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: NULL pointer");
-  if (cmp_kv && (!cu_seqlens_cmp || !d_cmp_kv)) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: cmp_kv needs cu_seqlens_cmp and d_cmp_kv");
-  if (cmp_idx && !cmp_kv) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: cmp_idx given without cmp_kv");
-  if (cmp_idx && topk < 1) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: topk must be >= 1 with cmp_idx");
-  if (sinks && !d_sinks) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: sinks need d_sinks");
-  if (cmp_l1 && cmp_slots < 1) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: cmp_l1 needs cmp_slots >= 1");
-  if (B < 1 || Tq < 0 || Tkv < 0 || Tc < 0 || H < 1 || d < 1 || cmp_ratio < 1 || global_start < 0 ||
-      max_seqlen_kv < 0 || cmp_slots < 0)
-    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: invalid size or parameter");
-  if (!window_fits(ori_win_left, ori_win_right, Tkv))
-    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: window sides must be >= 0 with Tkv + sides < 2^31");
-  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
-    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: softmax_scale (%g) must be positive and finite",
-                static_cast<double>(softmax_scale));
-  if (static_cast<long long>(global_start) + Tq > Tkv)
-    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: global_start + Tq exceeds Tkv");
-  if (!dtype_ok(dtype)) return fail(CSA_EINVAL, "csa_sparse_mla_bwd: unknown dtype %d", dtype);
-  if (cmp_idx && topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_bwd: topk %d > %d", topk, kMaxTopk);
-  if (!csa::mla_bwd_shape_supported(H, d, dtype))
-    return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_bwd: no kernel for H=%d d=%d dtype=%d", H, d, dtype);
-  const int cap = bwd_key_cap(ori_win_left, ori_win_right, cmp_kv, cmp_idx, topk, max_seqlen_kv, cmp_ratio);
-  const int nvis_cap = bwd_nvis_cap(cmp_kv, cmp_idx, max_seqlen_kv, cmp_ratio);
-  const int64_t need = static_cast<int64_t>(csa::mla_bwd_workspace_bytes(Tq, cap, nvis_cap));
-  if (workspace_bytes < need)
-    return fail(CSA_EINVAL, "csa_sparse_mla_bwd: workspace of %lld bytes < %lld needed",
-                static_cast<long long>(workspace_bytes), static_cast<long long>(need));
-  return hip_status(csa::launch_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, cmp_kv ? Tc : 0,
-                                               cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
-                                               cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks,
-                                               softmax_scale, out, lse, dout, dq, d_ori_kv,
-                                               cmp_kv ? d_cmp_kv : nullptr, d_sinks, ori_l1, cmp_l1, cmp_slots, cap,
-                                               nvis_cap, workspace,
-                                               static_cast<hipStream_t>(stream)),
-                    "csa_sparse_mla_bwd");
+  return bwd_call("csa_sparse_mla_bwd", false, q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d, dtype,
+                  cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left,
+                  ori_win_right, max_seqlen_kv, sinks, softmax_scale, out, lse, dout, dq, d_ori_kv, d_cmp_kv, d_sinks,
+                  ori_l1, cmp_l1, cmp_slots, workspace, workspace_bytes, stream);
+}
+
+int csa_sparse_mla_bwd_deterministic(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
+                                     int32_t topk, int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d,
+                                     int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
+                                     const int32_t* cu_seqlens_cmp, int32_t B, int32_t global_start,
+                                     int32_t cmp_ratio, int32_t ori_win_left, int32_t ori_win_right,
+                                     int32_t max_seqlen_kv, const float* sinks, float softmax_scale, const void* out,
+                                     const float* lse, const void* dout, void* dq, float* d_ori_kv, float* d_cmp_kv,
+                                     float* d_sinks, float* ori_l1, float* cmp_l1, int32_t cmp_slots,
+                                     void* workspace, int64_t workspace_bytes, csa_stream_t stream) {
+  return bwd_call("csa_sparse_mla_bwd_deterministic", true, q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, Tc, H, d,
+                  dtype, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio, ori_win_left,
+                  ori_win_right, max_seqlen_kv, sinks, softmax_scale, out, lse, dout, dq, d_ori_kv, d_cmp_kv, d_sinks,
+                  ori_l1, cmp_l1, cmp_slots, workspace, workspace_bytes, stream);
 }
 
 int64_t csa_indexer_kl_grad_workspace_bytes(int32_t Tq, int32_t topk, int32_t max_seqlen_kv, int32_t cmp_ratio) {

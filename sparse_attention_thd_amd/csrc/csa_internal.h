@@ -40,7 +40,7 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
                                  int max_seqlen_kv, const float* sinks, float scale, const void* out,
                                  const float* lse, const void* dout, void* dq, float* d_ori, float* d_cmp,
                                  float* d_sinks, float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap,
-                                 int nvis_cap, void* workspace, hipStream_t s);
+                                 int nvis_cap, void* workspace, bool deterministic, hipStream_t s);
 
 hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_cmp, const int32_t* cmp_idx,
                                   const float* attn_l1, int topk, int Tq, int Tc, const int32_t* cu_q,
@@ -63,5 +63,7 @@ bool indexer_shape_supported(int H_I, int d_I, int dtype);
 bool mla_shape_supported(int H, int d, int dtype);
 bool mla_bwd_shape_supported(int H, int d, int dtype);
 size_t mla_bwd_workspace_bytes(int Tq, int key_cap, int nvis_cap);
+// Partial row-gradient tiles of the deterministic backward (an upper bound from the sizes).
+size_t mla_bwd_partial_bytes(int Tq, int B, int wl, int wr, int Tkv, bool has_cmp, int max_seqlen_kv, int r);
 
 }  // namespace csa

@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ dout, int Tq, const void* ws_base, int nslot,
     int nvis_cap, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv,
     const int32_t* __restrict__ cu_cmp, int B, int global_start, int r, int wl, int wr, int Tc, int sparse,
-    float* __restrict__ d_ori, float* __restrict__ d_cmp) {
+    float* __restrict__ d_ori, float* __restrict__ d_cmp, float* __restrict__ part, int items_per_chunk) {
   __shared__ __attribute__((aligned(1024))) unsigned char stg[2 * kStage];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
   // consecutive workgroup slots there: two per item (the dims halves).
   const int x = static_cast<int>(blockIdx.x);
   const int xcd = x & 7, slot = x >> 3;
-  int seg = -1, chunk = 0, local = 0, off = 0, g_base = 0;
+  int seg = -1, chunk = 0, local = 0, off = 0, g_base = 0, gchunk = 0;
   for (int b = 0; b < B && seg < 0; ++b) {
     const int nch = seg_chunks(b, cu_q, cu_kv);
     for (int cbase = 0; cbase < nch && seg < 0; cbase += 64) {
@@ -523,6 +523,7 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
         const int src = __builtin_ctzll(hit);
         seg = b;
         chunk = cbase + src;
+        gchunk = g_base + chunk;
         local = slot - __shfl(incl - v, src, 64);
       }
       off = __shfl(incl, 63, 64);
@@ -532,7 +533,12 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
   seg = __builtin_amdgcn_readfirstlane(seg);
   if (seg < 0) return;
   chunk = __builtin_amdgcn_readfirstlane(chunk);
+  gchunk = __builtin_amdgcn_readfirstlane(gchunk);
   local = __builtin_amdgcn_readfirstlane(local);
+  // deterministic mode: this item's tile goes to its own slot of the partial buffer
+  float* tile = (part != nullptr)
+                    ? part + (static_cast<long long>(gchunk) * items_per_chunk + local) * (static_cast<long long>(kGK) * 256)
+                    : nullptr;
   const ChunkGroup gr = chunk_group(seg, chunk, cu_q, cu_kv, cu_cmp, global_start, r, wl, wr, Tc);
   const int half = local & 1, u = local >> 1;
   const int s = cu_kv[seg], e = cu_kv[seg + 1];
@@ -553,7 +559,13 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
     i0 = static_cast<int>(max(static_cast<long long>(gr.T0), first)) - global_start;
     i1 = gr.T1 - global_start + 1;
   }
-  if (i0 >= i1) return;
+  if (i0 >= i1) {
+    if (tile != nullptr) {  // no query meets these keys: the slot holds zeros
+      for (int k = tid; k < (key_end - key0) * 64; k += kDkvThreads)
+        reinterpret_cast<float4*>(tile)[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
 
   const BwdWorkspace ws = ws_layout(const_cast<void*>(ws_base), Tq, nslot, nvis_cap);
   const uint32_t sb = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(CSA_LDS(stg)));
@@ -724,6 +736,21 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---- C (32x32 blocks: lane l holds column l % 32, rows 8 (j / 4) + 4 (l / 32) + j % 4)
+  if (tile != nullptr) {
+    // deterministic mode: plain stores of the whole tile (rows below key_end), zeros included
+    const int tcol = 128 * wb + (lane & 31);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kr = 32 * (wa + 4 * kb) + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+        if (key0 + kr >= key_end) continue;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) tile[kr * 256 + tcol + 32 * db] = acc[kb][db][j];
+      }
+    }
+    return;
+  }
   float* dst = win ? d_ori : d_cmp;
   const int col = half * 256 + 128 * wb + (lane & 31);
 #pragma unroll
@@ -737,6 +764,82 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int db = 0; db < 4; ++db) atomicAdd(dst + static_cast<long long>(key) * 512 + col + 32 * db, acc[kb][db][j]);
     }
   }
+}
+
+// ----------------------------------------------------------------------------- deterministic row gradients
+
+// One workgroup of 128 threads per gradient row (window rows 0 .. Tkv - 1, then
+// compressed rows 0 .. Tc - 1); thread l sums dims 4 l .. 4 l + 3 over the work items
+// whose key tile holds the row, in ascending query-chunk order (the same items the
+// atomic mode adds, in a fixed order), and stores the row.
+__global__ __launch_bounds__(128) void mla_bwd_dkv_reduce_kernel(
+    const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp, int B,
+    int Tkv, int Tc, int global_start, int r, int wl, int wr, const float* __restrict__ part, int items_per_chunk,
+    float* __restrict__ d_ori, float* __restrict__ d_cmp) {
+  const int row = static_cast<int>(blockIdx.x);
+  const int tid = threadIdx.x;
+  const bool win = row < Tkv;
+  const int key = win ? row : row - Tkv;
+  // segment of the row: cu_kv for latent rows, cu_cmp (bounded by Tc) for compressed rows
+  const int32_t* cu = win ? cu_kv : cu_cmp;
+  int lo = 0, hi = B - 1;  // largest b with cu[b] <= key
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= key) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  const bool inside = key < cu[b + 1];
+  if (inside) {
+    int g_base = 0;
+    for (int bb = 0; bb < b; ++bb) g_base += seg_chunks(bb, cu_q, cu_kv);
+    const int qa = cu_q[b], qb = cu_q[b + 1], s = cu_kv[b];
+    const int nch = seg_chunks(b, cu_q, cu_kv);
+    int c_lo = 0, c_hi = -1;
+    if (nch > 0) {
+      if (win) {
+        // queries t with t - wl <= key <= t + wr
+        const int i_lo = max(qa, key - wr - global_start), i_hi = min(qb - 1, key + wl - global_start);
+        if (i_lo <= i_hi) {
+          c_lo = (i_lo - qa) / kQCH;
+          c_hi = (i_hi - qa) / kQCH;
+        }
+      } else {
+        // compressed row jl of the segment is visible from segment position (jl + 1) r - 1
+        const int jl = key - cu_cmp[b];
+        const long long i_first = static_cast<long long>(s) + static_cast<long long>(jl + 1) * r - 1 - global_start;
+        if (i_first <= qb - 1) {
+          c_lo = static_cast<int>((max(i_first, static_cast<long long>(qa)) - qa) / kQCH);
+          c_hi = nch - 1;
+        }
+      }
+    }
+    const int dim = 4 * tid;
+    const int half = dim >> 8;
+    for (int c = c_lo; c <= c_hi; ++c) {
+      const ChunkGroup gr = chunk_group(b, c, cu_q, cu_kv, cu_cmp, global_start, r, wl, wr, Tc);
+      int u, key0;
+      if (win) {
+        if (key < gr.k_lo || key > gr.k_hi) continue;
+        u = (key - gr.k_lo) / kGK;
+        key0 = gr.k_lo + kGK * u;
+      } else {
+        const int jl = key - cu_cmp[b];
+        if (jl / kGK >= gr.n_c) continue;
+        u = gr.n_w + jl / kGK;
+        key0 = cu_cmp[b] + kGK * (jl / kGK);
+      }
+      const float* t = part + (static_cast<long long>(g_base + c) * items_per_chunk + 2 * u + half) *
+                                  (static_cast<long long>(kGK) * 256);
+      const float4 v = *reinterpret_cast<const float4*>(t + (key - key0) * 256 + (dim & 255));
+      sum.x += v.x;
+      sum.y += v.y;
+      sum.z += v.z;
+      sum.w += v.w;
+    }
+  }
+  float* dst = win ? d_ori : d_cmp;
+  reinterpret_cast<float4*>(dst + static_cast<long long>(key) * 512)[tid] = sum;
 }
 
 // ----------------------------------------------------------------------------- sinks
@@ -773,16 +876,27 @@ size_t mla_bwd_workspace_bytes(int Tq, int key_cap, int nvis_cap) {
   return ws_bytes(Tq, slots_per_query(key_cap), nvis_cap);
 }
 
+size_t mla_bwd_partial_bytes(int Tq, int B, int wl, int wr, int Tkv, bool has_cmp, int max_seqlen_kv, int r) {
+  const long long wl_c = min(wl, Tkv), wr_c = min(wr, Tkv);
+  const long long seg_max = max(1, max_seqlen_kv);
+  const long long groups = (static_cast<long long>(Tq) + kQCH - 1) / kQCH + B;
+  const long long n_w = min(static_cast<long long>(kQCH) - 1 + wl_c + wr_c, seg_max - 1) / kGK + 1;
+  const long long n_c = has_cmp ? (seg_max / r + kGK - 1) / kGK : 0;
+  return static_cast<size_t>(groups * 2 * (n_w + n_c)) * kGK * 256 * sizeof(float);
+}
+
 hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx,
                                  int topk, int Tq, int Tkv, int Tc, const int32_t* cu_q, const int32_t* cu_kv,
                                  const int32_t* cu_cmp, int B, int global_start, int r, int wl, int wr,
                                  int max_seqlen_kv, const float* sinks, float scale, const void* out,
                                  const float* lse, const void* dout, void* dq, float* d_ori, float* d_cmp,
                                  float* d_sinks, float* ori_l1, float* cmp_l1, int cmp_slots, int key_cap,
-                                 int nvis_cap, void* workspace, hipStream_t s) {
+                                 int nvis_cap, void* workspace, bool deterministic, hipStream_t s) {
   const int W = wl + wr + 1;
-  zero(d_ori, static_cast<long long>(Tkv) * 512, s);
-  zero(d_cmp, static_cast<long long>(Tc) * 512, s);
+  if (!deterministic) {  // the deterministic reduce writes every row itself
+    zero(d_ori, static_cast<long long>(Tkv) * 512, s);
+    zero(d_cmp, static_cast<long long>(Tc) * 512, s);
+  }
   zero(ori_l1, static_cast<long long>(Tq) * W, s);
   zero(cmp_l1, static_cast<long long>(Tq) * cmp_slots, s);
   if (d_sinks != nullptr && (Tq == 0 || sinks == nullptr)) zero(d_sinks, 64, s);
@@ -807,10 +921,18 @@ hipError_t launch_sparse_mla_bwd(const void* q, const void* ori_kv, const void* 
   const long long n_c = (cmp_kv != nullptr) ? (seg_max / r + kGK - 1) / kGK : 0;
   const long long items = (groups + 7) / 8 * 2 * (n_w + n_c) * 8;
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int per_chunk = static_cast<int>(2 * (n_w + n_c));
+  float* part = deterministic ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) +
+                                                         ws_bytes(Tq, nslot, nvis_cap))
+                              : nullptr;
   hipLaunchKernelGGL(mla_bwd_dkv_kernel, dim3(static_cast<unsigned>(items)), dim3(kDkvThreads), 0, s, q16, d16, Tq,
                      static_cast<const void*>(workspace), nslot, nvis_cap, cu_q, cu_kv,
                      cmp_kv != nullptr ? cu_cmp : nullptr, B, global_start, r, wl_c, wr_c, Tc,
-                     cmp_idx != nullptr ? 1 : 0, d_ori, d_cmp);
+                     cmp_idx != nullptr ? 1 : 0, d_ori, d_cmp, part, per_chunk);
+  if (deterministic && Tkv + Tc > 0)
+    hipLaunchKernelGGL(mla_bwd_dkv_reduce_kernel, dim3(static_cast<unsigned>(Tkv + Tc)), dim3(128), 0, s, cu_q, cu_kv,
+                       cmp_kv != nullptr ? cu_cmp : nullptr, B, Tkv, Tc, global_start, r, wl_c, wr_c, part, per_chunk,
+                       d_ori, d_cmp);
   if (d_sinks != nullptr && sinks != nullptr)
     hipLaunchKernelGGL(mla_bwd_sink_kernel, dim3(64), dim3(kThreads), 0, s, static_cast<const void*>(workspace), Tq,
                        nslot, nvis_cap, d_sinks);

@@ -185,6 +185,44 @@ def test_sparse_mla_bwd_workspace_size_formula():
     assert n_wide == total(2, 320 * 256 + 4 + 256)
 
 
+def _mla_bwd_det(**kw):
+    a = dict(q=FAKE, kv=FAKE, ckv=FAKE, cidx=FAKE, topk=512, Tq=8, Tkv=8, Tc=2, H=64, d=512, dtype=1, cu_q=FAKE,
+             cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, wl=127, wr=0, maxlen=8, sinks=FAKE, scale=0.04, out=FAKE,
+             lse=FAKE, dout=FAKE, dq=FAKE, dkv=FAKE, dcmp=FAKE, dsinks=FAKE, ol1=None, cl1=None, slots=0,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return LIB.csa_sparse_mla_bwd_deterministic(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), EINVAL), (dict(ws=None), EINVAL), (dict(dkv=None), EINVAL), (dict(B=0), EINVAL),
+    (dict(topk=0), EINVAL), (dict(scale=0.0), EINVAL), (dict(ws_bytes=1024), EINVAL), (dict(H=16), EUNSUP),
+])
+def test_sparse_mla_bwd_deterministic_rejects(kw, code):
+    assert _mla_bwd_det(**kw) == code
+    assert b"csa_sparse_mla_bwd_deterministic" in LIB.csa_last_error()
+
+
+def test_sparse_mla_bwd_deterministic_needs_the_partial_tiles():
+    # the atomic call's workspace is not enough: the per-item tiles come on top of it
+    base = LIB.csa_sparse_mla_bwd_workspace_bytes(8, 127, 0, FAKE, FAKE, 512, 8, 4)
+    assert _mla_bwd_det(ws_bytes=base) == EINVAL
+    assert b"workspace" in LIB.csa_last_error()
+
+
+def test_sparse_mla_bwd_deterministic_workspace_size_formula():
+    # the atomic workspace + (ceil(Tq / 128) + B) query chunks x 2 (n_w + n_c) items x 256 x 256 float32,
+    # n_w = min(127 + wl + wr, max_seqlen_kv - 1) // 256 + 1, n_c = ceil(floor(max_seqlen_kv / r) / 256)
+    base = LIB.csa_sparse_mla_bwd_workspace_bytes(10, 127, 0, FAKE, FAKE, 512, 4039, 4)
+    n = LIB.csa_sparse_mla_bwd_deterministic_workspace_bytes(10, 1, 127, 0, FAKE, FAKE, 512, 4039, 4)
+    assert n == base + (1 + 1) * 2 * (1 + 4) * 256 * 256 * 4
+    base2 = LIB.csa_sparse_mla_bwd_workspace_bytes(300, 127, 0, None, None, 0, 700, 4)  # window only
+    n2 = LIB.csa_sparse_mla_bwd_deterministic_workspace_bytes(300, 3, 127, 0, None, None, 0, 700, 4)
+    assert n2 == base2 + (3 + 3) * 2 * (1 + 0) * 256 * 256 * 4
+    assert LIB.csa_sparse_mla_bwd_deterministic_workspace_bytes(10, 0, 127, 0, FAKE, FAKE, 512, 4039, 4) == -1
+    assert LIB.csa_sparse_mla_bwd_deterministic_workspace_bytes(-1, 1, 127, 0, None, None, 0, 0, 4) == -1
+
+
 def _kl(**kw):
     a = dict(q=FAKE, w=FAKE, k=FAKE, cidx=FAKE, p=FAKE, topk=512, Tq=8, Tc=2, H=64, d=128, dtype=1, cu_q=FAKE,
              cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, maxlen=8, scale=1.0, dq=FAKE, dw=FAKE, dk=FAKE, loss=None,

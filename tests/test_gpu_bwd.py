@@ -63,9 +63,10 @@ def _small(name):
     raise KeyError(name)
 
 
-def _run_bwd(pack, plan, seed):
-    """csa_sparse_mla_bwd on the forward's results; returns host copies, the dout used,
-    whether the layer attends to every visible compressed row, and the slot count."""
+def _run_bwd(pack, plan, seed, deterministic=False):
+    """csa_sparse_mla_bwd (or its deterministic form) on the forward's results; returns host
+    copies, the dout used, whether the layer attends to every visible compressed row, and
+    the slot count."""
     import sparse_attention_thd_amd as s
     rng = np.random.default_rng(seed)
     T, H, d = pack.Tq, pack.H, pack.d
@@ -77,8 +78,13 @@ def _run_bwd(pack, plan, seed):
     W = pack.ori_win_left + pack.ori_win_right + 1
     slots = topk if cmp_idx is not None else (max(1, pack.max_seqlen_kv // pack.cmp_ratio) if attend_all else 0)
     Tc = 0 if cmp_kv is None else cmp_kv.shape[0]
-    nbytes = s.csa_sparse_mla_bwd_workspace_bytes(T, pack.ori_win_left, pack.ori_win_right, cmp_kv, cmp_idx, topk,
-                                                  pack.max_seqlen_kv, pack.cmp_ratio)
+    if deterministic:
+        nbytes = s.csa_sparse_mla_bwd_deterministic_workspace_bytes(T, L.B, pack.ori_win_left, pack.ori_win_right,
+                                                                    cmp_kv, cmp_idx, topk, pack.max_seqlen_kv,
+                                                                    pack.cmp_ratio)
+    else:
+        nbytes = s.csa_sparse_mla_bwd_workspace_bytes(T, pack.ori_win_left, pack.ori_win_right, cmp_kv, cmp_idx,
+                                                      topk, pack.max_seqlen_kv, pack.cmp_ratio)
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
     dq = torch.empty_like(plan.out)
     d_ori = torch.empty((L.Tkv, d), dtype=torch.float32, device="cuda")
@@ -86,13 +92,14 @@ def _run_bwd(pack, plan, seed):
     d_sinks = torch.empty(H, dtype=torch.float32, device="cuda") if pack.sinks is not None else None
     ori_l1 = torch.empty((T, W), dtype=torch.float32, device="cuda")
     cmp_l1 = torch.empty((T, slots), dtype=torch.float32, device="cuda") if slots else None
-    print(f"[case] {pack.name}: csa_sparse_mla_bwd Tq={T} Tc={Tc} topk={topk} attend_all={attend_all} "
+    call = s.csa_sparse_mla_bwd_deterministic if deterministic else s.csa_sparse_mla_bwd
+    print(f"[case] {pack.name}: {call.__name__} Tq={T} Tc={Tc} topk={topk} attend_all={attend_all} "
           f"workspace={nbytes / 2**20:.1f} MiB", flush=True)
-    s.csa_sparse_mla_bwd(to_device(pack.q), to_device(pack.ori_kv), cmp_kv, cmp_idx, topk, T, L.Tkv, Tc, H, d,
-                         L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp if cmp_kv is not None else None, L.B,
-                         L.global_start, pack.cmp_ratio, pack.ori_win_left, pack.ori_win_right, pack.max_seqlen_kv,
-                         to_device(pack.sinks), pack.softmax_scale, plan.out, plan.lse, dout, dq, d_ori, d_cmp,
-                         d_sinks, ori_l1, cmp_l1, slots, ws)
+    call(to_device(pack.q), to_device(pack.ori_kv), cmp_kv, cmp_idx, topk, T, L.Tkv, Tc, H, d,
+         L.cu_seqlens_q, L.cu_seqlens_kv, plan.cu_seqlens_cmp if cmp_kv is not None else None, L.B,
+         L.global_start, pack.cmp_ratio, pack.ori_win_left, pack.ori_win_right, pack.max_seqlen_kv,
+         to_device(pack.sinks), pack.softmax_scale, plan.out, plan.lse, dout, dq, d_ori, d_cmp,
+         d_sinks, ori_l1, cmp_l1, slots, ws)
     torch.cuda.synchronize()
     got = dict(dq=cpu(dq), d_ori_kv=cpu(d_ori), d_cmp_kv=cpu(d_cmp), d_sinks=cpu(d_sinks), ori_l1=cpu(ori_l1),
                cmp_l1=cpu(cmp_l1))
@@ -242,3 +249,33 @@ def test_backward_empty_query_slice():
     torch.cuda.synchronize()
     for t in (d_ori, d_cmp, d_s):
         assert not t.isnan().any() and not t.any()
+
+
+@pytest.mark.parametrize("name", ["select16", "edges", "hca_small", "cp_small", "win_right", "no_compress",
+                                  "many_segs", "topk1024", "pack16k"])
+def test_deterministic_backward_is_bit_reproducible(name):
+    """csa_sparse_mla_bwd_deterministic: two calls give identical outputs to the bit; dq, the
+    probabilities and d_sinks equal the atomic call's exactly (the same kernels), the row
+    gradients equal it up to float32 summation order, and they meet the oracle's bounds
+    (every query, through the atomic call they match)."""
+    pack = make_pack("pack16k") if name == "pack16k" else _small(name)
+    plan = run_pack(pack)
+    a, dout, attend_all, slots = _run_bwd(pack, plan, seed=71)
+    d1, _, _, _ = _run_bwd(pack, plan, seed=71, deterministic=True)
+    d2, _, _, _ = _run_bwd(pack, plan, seed=71, deterministic=True)
+    for k in d1:
+        if d1[k] is None:
+            continue
+        assert np.array_equal(d1[k], d2[k]), f"{k} differs between two deterministic calls"
+    for k in ("dq", "ori_l1", "cmp_l1", "d_sinks"):
+        if a[k] is not None:
+            assert np.array_equal(a[k], d1[k]), f"{k} differs from the atomic call"
+    for k in ("d_ori_kv", "d_cmp_kv"):
+        if a[k] is None:
+            continue
+        ref = np.asarray(a[k], np.float64)
+        got = np.asarray(d1[k], np.float64)
+        scale = max(float(np.abs(ref).max()), 1e-30)
+        err = float(np.abs(got - ref).max())
+        print(f"    {k}: max|det - atomic| = {err:.3e} (|ref|inf {scale:.3e})", flush=True)
+        assert err <= 1e-5 * scale, k
