@@ -16,11 +16,19 @@
  * Conventions shared by every call
  * --------------------------------
  * - Every tensor pointer is DEVICE memory owned by the caller, contiguous,
- *   row-major.  The library allocates nothing and keeps no state between calls.
+ *   row-major.  The library allocates nothing and keeps no state between calls
+ *   (besides two device arrays it holds per GPU: the workspace of
+ *   csa_indexer_kl_grad_noalloc and the 8-byte result of csa_validate_topk_rows).
  * - Every call enqueues its kernels on `stream` (a hipStream_t; NULL = the null
  *   stream) and returns without synchronising.  Outputs are valid once the
  *   stream reaches that point.
- * - Host integers size the grids, so no call copies anything device -> host.
+ * - Host integers size the grids, so no call copies anything device -> host (the
+ *   two csa_validate_* checks excepted: they are synchronous).
+ * - Debug build: the library built with CSA_DEBUG defined (libcsa_debug.so, from
+ *   `build.py --debug`; csa_version() ends in "+debug") runs csa_validate_topk_rows
+ *   on the index rows of csa_sparse_mla_bwd(_deterministic), csa_indexer_kl_grad(_noalloc)
+ *   and csa_sparse_mla_fwd with CSA_IDX_TOPK before launching, synchronising the
+ *   stream, and fails those calls with CSA_EINVAL naming the first bad query.
  * - THD layout: `cu_seqlens_kv` [B+1] int32 holds stream-absolute segment
  *   bounds (the prefix of the stream whose KV is resident; a context-parallel
  *   rank passes the global segmentation truncated at its KV prefix end).
@@ -411,6 +419,22 @@ int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k
                         int32_t Tq, int32_t Tkv, int32_t global_start, int32_t max_seqlen_kv,
                         int32_t cmp_ratio, const int32_t* cu_seqlens_cmp, const int32_t* cmp_residual,
                         csa_stream_t stream);
+
+/*
+ * csa_validate_topk_rows - synchronous check of the index rows the sparse-MLA
+ * backward and the indexer KL gradient assume, and csa_sparse_mla_fwd's
+ * CSA_IDX_TOPK kind declares ([HP] 1. npu_lightning_indexer: the top-k of each
+ * query's visible candidates): every valid entry (>= 0) of cmp_idx[i, :] is a
+ * compressed row visible to query i, i.e. in [cu_seqlens_cmp[b], cu_seqlens_cmp[b]
+ * + min(floor((p + 1) / cmp_ratio), len_b / cmp_ratio, Tc - cu_seqlens_cmp[b])) for
+ * its segment b and position p, and no entry repeats another of the same row.  One
+ * GPU workgroup per query (an LDS bitmap of the visible rows); blocks on `stream`.
+ * Returns CSA_OK, or CSA_EINVAL naming the first bad query and entry; CSA_EINVAL also
+ * for invalid arguments and for a query with more than 32768 visible rows (not checked).
+ */
+int csa_validate_topk_rows(const int32_t* cmp_idx, int32_t topk, int32_t Tq, int32_t Tc,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp,
+                           int32_t B, int32_t global_start, int32_t cmp_ratio, csa_stream_t stream);
 
 #ifdef __cplusplus
 }

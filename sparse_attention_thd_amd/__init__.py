@@ -11,11 +11,12 @@ from ._lib import (CSA_IDX_ANY, CSA_IDX_TOPK, CsaError, csa_build_indices, csa_c
                    csa_indexer_kl_grad, csa_indexer_kl_grad_noalloc, csa_indexer_kl_grad_workspace_bytes,
                    csa_indexer_topk, csa_indexer_topk_workspace_bytes, csa_last_error, csa_sparse_mla_bwd,
                    csa_sparse_mla_bwd_deterministic, csa_sparse_mla_bwd_deterministic_workspace_bytes,
-                   csa_sparse_mla_bwd_workspace_bytes, csa_sparse_mla_fwd, csa_validate_layout, csa_version)
+                   csa_sparse_mla_bwd_workspace_bytes, csa_sparse_mla_fwd, csa_validate_layout,
+                   csa_validate_topk_rows, csa_version)
 from .api import CsaPlan, LayerCompressMode, LearnedCompressor, ThdLayout, csa_forward, layer_compress_mode
 
 __all__ = ["CSA_IDX_ANY", "CSA_IDX_TOPK", "CsaError", "CsaPlan", "LayerCompressMode", "LearnedCompressor", "ThdLayout", "csa_build_indices", "csa_compress",
            "csa_compress_learned", "csa_forward", "csa_indexer_kl_grad", "csa_indexer_kl_grad_noalloc", "csa_indexer_kl_grad_workspace_bytes", "csa_indexer_topk", "csa_indexer_topk_workspace_bytes",
            "csa_last_error", "csa_sparse_mla_bwd", "csa_sparse_mla_bwd_deterministic",
-           "csa_sparse_mla_bwd_deterministic_workspace_bytes", "csa_sparse_mla_bwd_workspace_bytes", "csa_sparse_mla_fwd", "csa_validate_layout",
+           "csa_sparse_mla_bwd_deterministic_workspace_bytes", "csa_sparse_mla_bwd_workspace_bytes", "csa_sparse_mla_fwd", "csa_validate_layout", "csa_validate_topk_rows",
            "csa_version", "layer_compress_mode"]

@@ -47,6 +47,7 @@ SIGNATURES = {
     "csa_indexer_kl_grad_noalloc": [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _I, _I, _I, _I,
                                     C.c_float, _P, _P, _P, _P, _P],
     "csa_validate_layout": [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P],
+    "csa_validate_topk_rows": [_P, _I, _I, _I, _P, _P, _P, _I, _I, _I, _P],
 }
 RESTYPES = {"csa_version": C.c_char_p, "csa_last_error": C.c_char_p, "csa_sparse_mla_bwd_workspace_bytes": C.c_int64,
             "csa_sparse_mla_bwd_deterministic_workspace_bytes": C.c_int64,
@@ -60,10 +61,12 @@ class CsaError(RuntimeError):
         self.code = code
 
 
-def _load() -> C.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python sparse_attention_thd_amd/build.py`")
-    lib = C.CDLL(LIB_PATH)
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Open a build of the library (the product one by default; DEBUG_LIB_PATH is the
+    CSA_DEBUG build) with the argument and result types of include/csa.h."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python sparse_attention_thd_amd/build.py`")
+    lib = C.CDLL(path)
     for name, args in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.argtypes = args
@@ -71,7 +74,8 @@ def _load() -> C.CDLL:
     return lib
 
 
-LIB = _load()
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa_debug.so")
+LIB = load()
 
 
 def _check(code: int) -> None:
@@ -304,3 +308,12 @@ def csa_validate_layout(cu_seqlens_q, cu_seqlens_kv, B, Tq, Tkv, global_start, m
                                    max_seqlen_kv, cmp_ratio,
                                    _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, True, B + 1),
                                    _ptr(cmp_residual, "cmp_residual", i32, True, B), _stream(stream)))
+
+
+def csa_validate_topk_rows(cmp_idx, topk, Tq, Tc, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
+                           cmp_ratio, stream=None):
+    i32 = torch.int32
+    _check(LIB.csa_validate_topk_rows(
+        _ptr(cmp_idx, "cmp_idx", i32, Tq == 0, Tq * topk), topk, Tq, Tc,
+        _ptr(cu_seqlens_q, "cu_seqlens_q", i32, need=B + 1), _ptr(cu_seqlens_kv, "cu_seqlens_kv", i32, need=B + 1),
+        _ptr(cu_seqlens_cmp, "cu_seqlens_cmp", i32, need=B + 1), B, global_start, cmp_ratio, _stream(stream)))

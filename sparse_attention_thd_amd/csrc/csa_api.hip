@@ -38,7 +38,11 @@ constexpr int kMaxCandidates = 32768;
 
 extern "C" {
 
+#ifdef CSA_DEBUG
+const char* csa_version(void) { return "csa-gfx950 0.1.0+debug"; }
+#else
 const char* csa_version(void) { return "csa-gfx950 0.1.0"; }
+#endif
 
 const char* csa_last_error(void) { return g_last_error.c_str(); }
 
@@ -148,6 +152,35 @@ int csa_indexer_topk(const void* q_I, const void* w, const void* k_I_cmp, int32_
                     "csa_indexer_topk");
 }
 
+// Index rows: every valid entry a compressed row visible to its query, none repeated
+// (synchronises the stream; csa_validate_topk_rows, and every call taking top-k rows in
+// a CSA_DEBUG build).
+static int rows_check(const char* name, const int32_t* cmp_idx, int32_t topk, int32_t Tq, int32_t Tc,
+                      const int32_t* cu_q, const int32_t* cu_kv, const int32_t* cu_cmp, int32_t B,
+                      int32_t global_start, int32_t cmp_ratio, csa_stream_t stream) {
+  long long q = -1;
+  int entry = -1, reason = 0;
+  const hipError_t e = csa::check_topk_rows(cmp_idx, topk, Tq, cu_q, cu_kv, cu_cmp, B, global_start, cmp_ratio, Tc,
+                                            static_cast<hipStream_t>(stream), &q, &entry, &reason);
+  if (e != hipSuccess) return hip_status(e, name);
+  if (q < 0) return CSA_OK;
+  if (reason == 1)
+    return fail(CSA_EINVAL, "%s: query %lld, index entry %d is not a compressed row visible to the query", name, q,
+                entry);
+  if (reason == 2) return fail(CSA_EINVAL, "%s: query %lld, index entry %d repeats an earlier entry", name, q, entry);
+  return fail(CSA_EINVAL, "%s: query %lld sees more compressed rows than the check covers (32768)", name, q);
+}
+
+int csa_validate_topk_rows(const int32_t* cmp_idx, int32_t topk, int32_t Tq, int32_t Tc,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp,
+                           int32_t B, int32_t global_start, int32_t cmp_ratio, csa_stream_t stream) {
+  if (!cu_seqlens_q || !cu_seqlens_kv || !cu_seqlens_cmp || (Tq > 0 && !cmp_idx) || topk < 1 || Tq < 0 || Tc < 0 ||
+      B < 1 || global_start < 0 || cmp_ratio < 1)
+    return fail(CSA_EINVAL, "csa_validate_topk_rows: invalid argument");
+  return rows_check("csa_validate_topk_rows", cmp_idx, topk, Tq, Tc, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B,
+                    global_start, cmp_ratio, stream);
+}
+
 int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, const int32_t* cmp_idx, int32_t topk,
                        int32_t cmp_idx_kind, int32_t Tq, int32_t Tkv, int32_t Tc, int32_t H, int32_t d,
                        int32_t dtype, const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv,
@@ -174,6 +207,13 @@ int csa_sparse_mla_fwd(const void* q, const void* ori_kv, const void* cmp_kv, co
   if (cmp_idx && topk > kMaxTopk) return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_fwd: topk %d > %d", topk, kMaxTopk);
   if (!csa::mla_shape_supported(H, d, dtype))
     return fail(CSA_EUNSUPPORTED, "csa_sparse_mla_fwd: no kernel for H=%d d=%d dtype=%d", H, d, dtype);
+#ifdef CSA_DEBUG
+  if (cmp_idx && cmp_kv && cmp_idx_kind == CSA_IDX_TOPK) {
+    const int st = rows_check("csa_sparse_mla_fwd", cmp_idx, topk, Tq, Tc, cu_seqlens_q, cu_seqlens_kv,
+                              cu_seqlens_cmp, B, global_start, cmp_ratio, stream);
+    if (st != CSA_OK) return st;
+  }
+#endif
   return hip_status(csa::launch_sparse_mla(q, ori_kv, cmp_kv, cmp_idx, topk, cmp_idx_kind == CSA_IDX_TOPK, Tq,
                                            cmp_kv ? Tc : 0, H, d, dtype, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp,
                                            cmp_residual, B, global_start, cmp_ratio, ori_win_left, ori_win_right,
@@ -262,6 +302,13 @@ static int bwd_call(const char* name, bool deterministic, const void* q, const v
   if (workspace_bytes < need)
     return fail(CSA_EINVAL, "%s: workspace of %lld bytes < %lld needed", name,
                 static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+#ifdef CSA_DEBUG
+  if (cmp_idx && cmp_kv) {
+    const int st = rows_check(name, cmp_idx, topk, Tq, Tc, cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B,
+                              global_start, cmp_ratio, stream);
+    if (st != CSA_OK) return st;
+  }
+#endif
   return hip_status(csa::launch_sparse_mla_bwd(q, ori_kv, cmp_kv, cmp_idx, topk, Tq, Tkv, cmp_kv ? Tc : 0,
                                                cu_seqlens_q, cu_seqlens_kv, cu_seqlens_cmp, B, global_start,
                                                cmp_ratio, ori_win_left, ori_win_right, max_seqlen_kv, sinks,
@@ -327,6 +374,12 @@ int csa_indexer_kl_grad(const void* q_I, const void* w, const void* k_I_cmp, con
   if (workspace_bytes < need)
     return fail(CSA_EINVAL, "csa_indexer_kl_grad: workspace of %lld bytes < %lld needed",
                 static_cast<long long>(workspace_bytes), static_cast<long long>(need));
+#ifdef CSA_DEBUG
+  if (const int st = rows_check("csa_indexer_kl_grad", cmp_idx, topk, Tq, Tc, cu_seqlens_q, cu_seqlens_kv,
+                                cu_seqlens_cmp, B, global_start, cmp_ratio, stream);
+      st != CSA_OK)
+    return st;
+#endif
   return hip_status(csa::launch_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, cu_seqlens_q,
                                                 cu_seqlens_kv, cu_seqlens_cmp, B, global_start, cmp_ratio,
                                                 max_seqlen_kv, loss_scale, d_q_I, d_w, d_k_I_cmp, loss, nvis_cap,
@@ -358,6 +411,12 @@ int csa_indexer_kl_grad_noalloc(const void* q_I, const void* w, const void* k_I_
     return fail(CSA_EINVAL, "csa_indexer_kl_grad_noalloc: the call needs %zu bytes of scratch, more than the %zu "
                 "the library holds (Tq * (4 topk + 2 floor(max_seqlen_kv / cmp_ratio)) must stay within it)",
                 need, csa::kKlScratchBytes);
+#ifdef CSA_DEBUG
+  if (const int st = rows_check("csa_indexer_kl_grad_noalloc", cmp_idx, topk, Tq, Tc, cu_seqlens_q, cu_seqlens_kv,
+                                cu_seqlens_cmp, B, global_start, cmp_ratio, stream);
+      st != CSA_OK)
+    return st;
+#endif
   void* ws = nullptr;
   if (const int st = hip_status(csa::kl_scratch(&ws), "csa_indexer_kl_grad_noalloc"); st != CSA_OK) return st;
   return hip_status(csa::launch_indexer_kl_grad(q_I, w, k_I_cmp, cmp_idx, attn_l1, topk, Tq, Tc, cu_seqlens_q,

@@ -59,6 +59,12 @@ hipError_t launch_compress_learned(const void* x, int Tkv, int D, const void* wk
                                    const int32_t* cu_cmp, int B, void* out, int Tc_cap, hipStream_t s);
 bool learned_shape_supported(int D, int hd, int cmp_ratio, int overlap, int dtype);
 
+// First violation of the index-row precondition (visible, not repeated): bad_query -1 if none;
+// reason 1 not visible, 2 repeated, 3 too many visible rows to check.  Synchronises s.
+hipError_t check_topk_rows(const int32_t* rows, int topk, int Tq, const int32_t* cu_q, const int32_t* cu_kv,
+                           const int32_t* cu_cmp, int B, int global_start, int r, int Tc, hipStream_t s,
+                           long long* bad_query, int* bad_entry, int* reason);
+
 bool indexer_shape_supported(int H_I, int d_I, int dtype);
 bool mla_shape_supported(int H, int d, int dtype);
 bool mla_bwd_shape_supported(int H, int d, int dtype);

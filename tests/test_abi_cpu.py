@@ -39,6 +39,25 @@ def test_library_exports_every_declared_symbol():
         assert n in lib_mod.SIGNATURES, f"binding lacks {n}"
 
 
+def test_debug_build_exports_every_declared_symbol():
+    if not os.path.exists(lib_mod.DEBUG_LIB_PATH):
+        pytest.skip("libcsa_debug.so not built")
+    dbg = lib_mod.load(lib_mod.DEBUG_LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(dbg, n), n
+    assert dbg.csa_version().endswith(b"+debug")
+    assert not lib_mod.csa_version().endswith("+debug")
+
+
+@pytest.mark.parametrize("kw", [dict(cidx=None), dict(topk=0), dict(B=0), dict(r=0), dict(gs=-1), dict(Tc=-1),
+                                dict(cu_cmp=None), dict(Tq=-1)])
+def test_validate_topk_rows_rejects(kw):
+    a = dict(cidx=FAKE, topk=512, Tq=8, Tc=2, cu_q=FAKE, cu_kv=FAKE, cu_cmp=FAKE, B=1, gs=0, r=4, stream=None)
+    a.update(kw)
+    assert LIB.csa_validate_topk_rows(*a.values()) == EINVAL
+    assert b"csa_validate_topk_rows" in LIB.csa_last_error()
+
+
 def test_version_and_empty_error():
     assert lib_mod.csa_version().startswith("csa-gfx950")
 
