@@ -139,6 +139,26 @@ def test_kl_grad_matches_oracle(name):
     _check(pack, plan, _targets(plan, 200), 1.0 / pack.Tq)
 
 
+@pytest.mark.parametrize("name", ["select16", "long", "cp_small"])
+def test_kl_grad_unordered_rows_and_holes(name):
+    """Index rows in any order and with holes (-1) between entries: every third query's
+    row shuffled, every third a hole punched, the rest as the indexer wrote them (sorted),
+    so neighbouring queries pair sorted with sorted, sorted with unordered and unordered
+    with unordered lists."""
+    pack = _pack(name)
+    print(f"\n[case] {name} (unordered rows, holes): Tq={pack.Tq} -> forward on GPU", flush=True)
+    plan = run_pack(pack)
+    idx = cpu(plan.topk_idx).copy()
+    rng = np.random.default_rng(17)
+    for i in range(idx.shape[0]):
+        if i % 3 == 0:
+            rng.shuffle(idx[i])
+        elif i % 3 == 1:
+            idx[i, rng.integers(0, idx.shape[1])] = -1
+    plan.topk_idx = torch.from_numpy(idx).cuda()
+    _check(pack, plan, _targets(plan, 202), 1.0 / pack.Tq)
+
+
 def test_kl_grad_with_backward_targets():
     """The sparse-MLA backward's cmp_l1 (head-averaged probabilities) as the target."""
     import sparse_attention_thd_amd as s
