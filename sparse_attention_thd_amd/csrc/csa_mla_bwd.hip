@@ -669,23 +669,16 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
       for (int j = 0; j < 16; ++j) acc[kb][db][j] = 0.f;
   bool used[2] = {false, false};
 
-  // ---- pipeline: stage n + 1 is issued while stage n is multiplied.  The queries are
-  // swept from the last (i1 - 1) down: every item of a chunk ends at the chunk's last
-  // query while its first query depends on the tile, so all items of a chunk (both dims
-  // halves, every key tile, dealt to one XCD together) read the same q / dout rows at
-  // about the same time and share them in that XCD's L2.
-  const int nq = i1 - i0;
-  auto qat = [&](int k) { return i1 - 1 - k; };
+  // ---- pipeline: stage n + 1 is issued while stage n is multiplied
   int mp[4];
   const unsigned char* rowp[4];
-  load_map(qat(0), mp);
+  load_map(i0, mp);
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  QInfo cur = qinfo(qat(0));
-  slot_rows(qat(0), cur, mp, rowp);
-  stage(qat(0), 0, rowp, 0);
-  if (1 < nq) load_map(qat(1), mp);
-  for (int k = 0; k < nq; ++k) {
-    const int i = qat(k);
+  QInfo cur = qinfo(i0);
+  slot_rows(i0, cur, mp, rowp);
+  stage(i0, 0, rowp, 0);
+  if (i0 + 1 < i1) load_map(i0 + 1, mp);
+  for (int i = i0; i < i1; ++i) {
     // blocks of this wavefront with attended keys for query i
     bool act[2];
 #pragma unroll
@@ -697,18 +690,18 @@ __global__ __launch_bounds__(kDkvThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
 #pragma unroll
     for (int term = 0; term < 2; ++term) {
-      const int n = 2 * k + term;
+      const int n = 2 * (i - i0) + term;
       const int bf = n & 1;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // stage n (and the map entries of the next query) landed
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // stage n (and the map entries of query i + 1) landed
       tile_barrier();                      // every wavefront's part landed; buffer bf ^ 1 is free
       QInfo nxt = cur;
       if (term == 0) {
         stage(i, 1, rowp, bf ^ 1);
-      } else if (k + 1 < nq) {
-        nxt = qinfo(qat(k + 1));
-        slot_rows(qat(k + 1), nxt, mp, rowp);
-        stage(qat(k + 1), 0, rowp, bf ^ 1);
-        if (k + 2 < nq) load_map(qat(k + 2), mp);
+      } else if (i + 1 < i1) {
+        nxt = qinfo(i + 1);
+        slot_rows(i + 1, nxt, mp, rowp);
+        stage(i + 1, 0, rowp, bf ^ 1);
+        if (i + 2 < i1) load_map(i + 2, mp);
       }
       if (act[0] || act[1]) {
         const unsigned char* y = stg + bf * kStage;
