@@ -36,6 +36,10 @@ def _small(name):
         return pack_from_lengths("cp_small", [700, 1500, 900, 400], seed=8, q_rows=(1000, 2600), kv_rows=2600)
     if name == "win_right":
         return pack_from_lengths("win_right", [300, 411], seed=9, ori_win_left=20, ori_win_right=5, topk=32)
+    if name == "ratio3":       # ratios that are not powers of two: the mean's one rounding of sum / r
+        return pack_from_lengths("ratio3", [301, 700, 2, 130], seed=27, cmp_ratio=3, indexer=False)
+    if name == "ratio5":
+        return pack_from_lengths("ratio5", [17, 999, 4, 260], seed=28, cmp_ratio=5, indexer=False)
     if name == "no_compress":
         return pack_from_lengths("no_compress", [200, 333], seed=10, cmp_ratio=1, indexer=False)
     if name == "many_segs":    # more than 64 segments (segment search and bounds past one wavefront)
@@ -59,7 +63,8 @@ def _small(name):
 
 
 FULL = ["tiny", "single4k", "pack16k", "hca32k", "cp32k", "stress"]
-SMALL = ["edges", "select16", "long", "short_only", "hca_small", "cp_small", "win_right", "no_compress",
+SMALL = ["edges", "select16", "long", "short_only", "hca_small", "ratio3", "ratio5", "cp_small", "win_right",
+         "no_compress",
          "many_segs", "topk1024", "pair_long", "max_limits", "wide_window", "generic_f32", "generic_bf16"]
 ALL = SMALL + FULL
 
@@ -134,7 +139,7 @@ def test_compress_bitexact(name):
         np.testing.assert_array_equal(res["k_I_cmp"][:Tc].astype(np.float64), _oracle_cmp(res, "k_I"))
 
 
-INDEXER_CASES = [n for n in ALL if n not in ("hca32k", "hca_small", "no_compress")]
+INDEXER_CASES = [n for n in ALL if n not in ("hca32k", "hca_small", "ratio3", "ratio5", "no_compress")]
 
 
 @pytest.mark.parametrize("name", INDEXER_CASES)
