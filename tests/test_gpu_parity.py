@@ -44,6 +44,8 @@ def _small(name):
         return pack_from_lengths("no_compress", [200, 333], seed=10, cmp_ratio=1, indexer=False)
     if name == "many_segs":    # more than 64 segments (segment search and bounds past one wavefront)
         return pack_from_lengths("many_segs", [5 + (37 * k) % 120 for k in range(80)], seed=13, topk=32)
+    if name == "segs1100":     # more segments than the layout kernel stages in LDS (1024)
+        return pack_from_lengths("segs1100", [1 + (7 * k) % 13 for k in range(1100)], seed=29, topk=2)
     if name == "pair_long":    # candidate lists of 2048+: queries scored in pairs; odd count, pairs across segments
         return pack_from_lengths("pair_long", [8301, 5, 2, 777], seed=24)
     if name == "topk1024":     # top-k above 512: the larger kernel instances, ~500 selecting queries
@@ -65,7 +67,7 @@ def _small(name):
 FULL = ["tiny", "single4k", "pack16k", "hca32k", "cp32k", "stress"]
 SMALL = ["edges", "select16", "long", "short_only", "hca_small", "ratio3", "ratio5", "cp_small", "win_right",
          "no_compress",
-         "many_segs", "topk1024", "pair_long", "max_limits", "wide_window", "generic_f32", "generic_bf16"]
+         "many_segs", "segs1100", "topk1024", "pair_long", "max_limits", "wide_window", "generic_f32", "generic_bf16"]
 ALL = SMALL + FULL
 
 _cache = {}
