@@ -574,10 +574,8 @@ hipError_t launch_indexer_kl_grad(const void* q_I, const void* w, const void* k_
   const auto* q16 = static_cast<const uint16_t*>(q_I);
   const auto* w16 = static_cast<const uint16_t*>(w);
   const auto* k16 = static_cast<const uint16_t*>(k_cmp);
-#ifndef CSA_KL_KB
-#define CSA_KL_KB 2
-#endif
-  auto kq = (topk <= 2 * kThreads) ? kl_query_kernel<2, CSA_KL_KB> : kl_query_kernel<kMaxTopk / kThreads, 2>;
+  // two K stage buffers (a third measured slower)
+  auto kq = (topk <= 2 * kThreads) ? kl_query_kernel<2, 2> : kl_query_kernel<kMaxTopk / kThreads, 2>;
   hipLaunchKernelGGL(kq, dim3(Tq), dim3(kThreads), 0, s, q16, w16, k16, cmp_idx, attn_l1, topk, Tq, Tc, cu_q, cu_kv,
                      cu_cmp, B, global_start, r, loss_scale, static_cast<uint16_t*>(d_q), d_w, loss, workspace,
                      nvis_cap);
