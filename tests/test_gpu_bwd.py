@@ -50,6 +50,8 @@ def _small(name):
         return pack_from_lengths("win_right", [300, 411], seed=9, ori_win_left=20, ori_win_right=5, topk=32)
     if name == "no_compress":
         return pack_from_lengths("no_compress", [200, 333], seed=10, cmp_ratio=1, indexer=False)
+    if name == "ratio5":  # every visible compressed row attended, a ratio that is not a power of two
+        return pack_from_lengths("ratio5", [17, 999, 4, 260], seed=28, cmp_ratio=5, indexer=False)
     if name == "many_segs":
         return pack_from_lengths("many_segs", [5 + (37 * k) % 120 for k in range(80)], seed=13, topk=32)
     if name == "stress_small":  # peaky softmax (q, kv ~ N(0,1))
@@ -134,7 +136,7 @@ def _oracle(pack, tabs, plan, dout, attend_all, slots, queries=None):
                                  queries=queries)
 
 
-SMALL = ["select16", "edges", "long", "short_only", "hca_small", "cp_small", "win_right", "no_compress",
+SMALL = ["select16", "edges", "long", "short_only", "hca_small", "ratio5", "cp_small", "win_right", "no_compress",
          "many_segs", "stress_small", "no_sinks", "topk1024", "max_limits"]
 
 

@@ -142,12 +142,12 @@ def test_compress_identity_at_ratio_one():
     np.testing.assert_array_equal(oracle.compress(x, [0, 7, 23], 1), x)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(10))
 def test_compress_matches_cell_means_and_ignores_tails(seed):
     rng = np.random.default_rng(200 + seed)
     L = _rand_lengths(rng, 4, 1, 35)
     cu = _cu(L)
-    r = int(rng.choice([2, 4, 8]))
+    r = int(rng.choice([2, 3, 4, 5, 8]))
     x = rng.standard_normal((int(cu[-1]), 6))
     got = oracle.compress(x, cu, r)
     _, full, cells = _brute_layout(cu, cu, 0, int(cu[-1]), r, 0, 0)
