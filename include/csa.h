@@ -431,6 +431,9 @@ int csa_validate_layout(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k
  * GPU workgroup per query (an LDS bitmap of the visible rows); blocks on `stream`.
  * Returns CSA_OK, or CSA_EINVAL naming the first bad query and entry; CSA_EINVAL also
  * for invalid arguments and for a query with more than 32768 visible rows (not checked).
+ * The first violation is gathered in an 8-byte device word the library holds per GPU:
+ * checks that overlap on one GPU (two streams, or two host threads; also the debug
+ * build's checks inside other calls) race on it and may report each other's result.
  */
 int csa_validate_topk_rows(const int32_t* cmp_idx, int32_t topk, int32_t Tq, int32_t Tc,
                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, const int32_t* cu_seqlens_cmp,
