@@ -171,8 +171,6 @@ __device__ __forceinline__ void write_poisoned_row(int32_t* __restrict__ out_idx
   }
 }
 
-constexpr int kSThreads = 512;             // scoring workgroup: 8 wavefronts, one query each
-constexpr int kSWaves = kSThreads / 64;
 // Candidates per LDS chunk (rows of 256 B) are a template parameter CH of the scoring
 // kernel: 128 (half the barriers) for long candidate lists, 64 (half the tail of the last
 // chunk) for short ones.  CH / 16 MFMA blocks per chunk; each of the 8 wavefronts stages
@@ -449,19 +447,19 @@ __global__ __launch_bounds__(kThreads) void indexer_select_kernel(
 // ---- pieces of indexer_score_kernel (plain functions: a by-reference lambda closure
 // would escape through the barriers' memory clobbers and put its captures in scratch)
 
-// Stage chunk c of a group's key rows into LDS buffer at lds_buf: wavefront w stages rows
-// CH / 8 * w onward (CH / 32 1 KiB instructions of 4 rows); rows past the group's
-// nvmax candidates re-read its first row.
-template <int CH>
+// Stage chunk c of a group's key rows into LDS buffer at lds_buf: wavefront w of NW stages
+// rows CH / NW * w onward (CH / (4 NW) 1 KiB instructions of 4 rows); rows past the
+// group's nvmax candidates re-read its first row.
+template <int CH, int NW>
 __device__ __forceinline__ void score_stage(const uint16_t* __restrict__ k_cmp, int glo, int nvmax, int c,
                                             uint32_t lds_buf, int wave, int lane) {
 #pragma unroll
-  for (int v = 0; v < CH / 32; ++v) {
-    const int rr = (CH / kSWaves) * wave + 4 * v + (lane >> 4);
+  for (int v = 0; v < CH / (4 * NW); ++v) {
+    const int rr = (CH / NW) * wave + 4 * v + (lane >> 4);
     int cand = CH * c + rr;
     cand = (cand < nvmax) ? cand : 0;
     const uint16_t* src = k_cmp + static_cast<long long>(glo + cand) * 128 + kchunk(rr, lane & 15) * 8;
-    gather16_to_lds(src, lds_buf + static_cast<uint32_t>(((CH / kSWaves) * wave + 4 * v) * 256));
+    gather16_to_lds(src, lds_buf + static_cast<uint32_t>(((CH / NW) * wave + 4 * v) * 256));
   }
 }
 
@@ -523,14 +521,14 @@ __device__ __forceinline__ void score_interleave() {
 // are returned) gets the key of each candidate c < nv in keys[i * cap + c]; the queries of
 // one segment share each staged chunk of key rows.  Tiles run on XCDs in runs of kRun, so
 // a run's queries (the same segment, mostly) also share the key rows in one L2.
-template <int CH>
-__global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
+template <int CH, int NW>
+__global__ __launch_bounds__(64 * NW) void indexer_score_kernel(
     const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp, int Tq,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
     const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk, int score_all,
     int ntile, uint32_t* __restrict__ keys) {
   __shared__ __attribute__((aligned(1024))) unsigned char kst[kStages][CH * 256];
-  __shared__ int wseg[kSWaves], wlo[kSWaves], wnv[kSWaves];
+  __shared__ int wseg[NW], wlo[NW], wnv[NW];
   constexpr int NB = CH / 16;
   const int xcd = static_cast<int>(blockIdx.x) & 7, kk = static_cast<int>(blockIdx.x) >> 3;
   const int tile = ((kk / kRun) * 8 + xcd) * kRun + (kk % kRun);
@@ -538,7 +536,7 @@ __global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int i = 8 * tile + wave;
+  const int i = NW * tile + wave;
   if (lane == 0) {
     int seg = -1, lo = 0, nv = 0;
     if (i < Tq) {
@@ -582,7 +580,7 @@ __global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
     while (true) {
       int gseg = -1, glo = 0, nvmax = 0, mask = 0;
 #pragma unroll
-      for (int k = 0; k < kSWaves; ++k) {
+      for (int k = 0; k < NW; ++k) {
         const int sk = wseg[k];
         if (sk < 0 || ((done >> k) & 1)) continue;
         if (gseg < 0) {
@@ -598,8 +596,8 @@ __global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
       done |= mask;
       const bool mine = (mask >> wave) & 1;
       const int nch = (nvmax + CH - 1) / CH;
-      score_stage<CH>(k_cmp, glo, nvmax, 0, kbase, wave, lane);
-      if (nch > 1) score_stage<CH>(k_cmp, glo, nvmax, 1, kbase + CH * 256, wave, lane);
+      score_stage<CH, NW>(k_cmp, glo, nvmax, 0, kbase, wave, lane);
+      if (nch > 1) score_stage<CH, NW>(k_cmp, glo, nvmax, 1, kbase + CH * 256, wave, lane);
       // Software pipeline over 16-candidate blocks: block (c, jb) issues its 16 MFMAs into
       // acc0 / acc1 (alternately) while the VALU epilogue (ReLU, head weights, lane-group sum) of the
       // previous block runs on the other buffer, so the matrix core and the VALU overlap
@@ -622,14 +620,14 @@ __global__ __launch_bounds__(kSThreads) void indexer_score_kernel(
         // chunk c has landed: the only younger vector-memory loads are chunk c + 1's
         // (loads retire in order; key stores in between do not matter)
         if (c + 1 < nch) {
-          __builtin_amdgcn_s_waitcnt(0x0F70 | (CH / 32));  // vmcnt(CH / 32)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | (CH / (4 * NW)));  // vmcnt(CH / (4 NW))
         } else {
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         }
         // every wavefront's rows of chunk c are visible; every wavefront is done with
         // chunk c - 1, whose buffer chunk c + 2 refills
         tile_barrier();
-        if (c + 2 < nch) score_stage<CH>(k_cmp, glo, nvmax, c + 2, kbase + ((c + 2) % kStages) * CH * 256, wave, lane);
+        if (c + 2 < nch) score_stage<CH, NW>(k_cmp, glo, nvmax, c + 2, kbase + ((c + 2) % kStages) * CH * 256, wave, lane);
         if (mine && my_nv > CH * c) {
           const unsigned char* kb = kst[bf];
           score_read_kf(kb, 0, n, g, kf0);
@@ -720,15 +718,21 @@ hipError_t launch_indexer_topk(const void* q_I, const void* w, const void* k_cmp
   size_t lds = static_cast<size_t>(cap) * 4;
   const dim3 grid(Tq), block(kThreads);
   if (mfma) {
-    const int ntile = (Tq + kSWaves - 1) / kSWaves;
-    const int runs = (ntile + 8 * kRun - 1) / (8 * kRun);
     uint32_t* keys = static_cast<uint32_t*>(workspace);
-    // long candidate lists: 128-row chunks (half the barriers); short ones: 64 (half the tail)
-    auto score_kernel = (cap >= 2048) ? indexer_score_kernel<128> : indexer_score_kernel<64>;
-    hipLaunchKernelGGL(score_kernel, dim3(static_cast<unsigned>(runs * 8 * kRun)), dim3(kSThreads), 0, s,
-                       static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
-                       static_cast<const uint16_t*>(k_cmp), Tq, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
-                       cap, Tc, topk, score != nullptr ? 1 : 0, ntile, keys);
+    auto launch_score = [&](auto kern, int nw) {
+      const int ntile = (Tq + nw - 1) / nw;
+      const int runs = (ntile + 8 * kRun - 1) / (8 * kRun);
+      hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(runs * 8 * kRun)), dim3(64 * nw), 0, s,
+                         static_cast<const uint16_t*>(q_I), static_cast<const uint16_t*>(w),
+                         static_cast<const uint16_t*>(k_cmp), Tq, cu_q, cu_kv, cu_cmp, residual, B, global_start, r,
+                         cap, Tc, topk, score != nullptr ? 1 : 0, ntile, keys);
+    };
+    // 64-row chunks and 8 queries per workgroup for every list length.  Measured: 128-row
+    // chunks on long lists are 2% slower on the 32k CP share (1.72 against 1.69 ms) and
+    // equal elsewhere; 4 queries per workgroup (two workgroups per CU) are 6% faster where
+    // few queries need scores (pack16k: 0.083 against 0.088 ms) but 2-6% slower where many
+    // do (4k pack, CP share), and which case holds is only known on the device.
+    launch_score(indexer_score_kernel<64, 8>, 8);
     // keys in registers up to 6144 candidates per query (one read of the workspace row),
     // streamed from the row on every pass beyond that
     const dim3 sgrid((Tq + kWaves - 1) / kWaves);
