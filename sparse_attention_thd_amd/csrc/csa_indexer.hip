@@ -402,8 +402,11 @@ __device__ __forceinline__ void wave_select_emit(const WaveKeys<KPL>& K, int top
 // One wavefront per query (4 per workgroup): the row of every query: poisoned, the
 // ascending list (with scores from the keys when asked), or the top-k of the keys the
 // scoring kernel wrote (KPL > 0: every candidate list fits 64 KPL keys in registers).
+// The 96-slot instance (lists of more than 4096 candidates) is held to 168 registers for
+// three wavefronts per SIMD (no spill): the 32k CP share's indexer call 1.71-1.73 ->
+// 1.61-1.63 ms; the smaller instances measured no change either way.
 template <int KPL>
-__global__ __launch_bounds__(kThreads) void indexer_select_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(KPL >= 96 ? 3 : 1))) void indexer_select_kernel(
     int Tq, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_kv, const int32_t* __restrict__ cu_cmp,
     const int32_t* __restrict__ residual, int B, int global_start, int r, int cap, int Tc, int topk,
     const uint32_t* __restrict__ keys, int32_t* __restrict__ idx, float* __restrict__ score) {
