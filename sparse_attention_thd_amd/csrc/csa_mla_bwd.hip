@@ -361,39 +361,45 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
     if (ntiles > 0) {
       lds_barrier();  // pairs with the dq wavefronts' last barrier
       if (want_l1) flush_l1(ntiles - 1);
+      lds_barrier();  // pairs with the dq wavefronts' staging barrier
     }
   } else {
-    // dq^T (dims x heads) += kv^T . (scale dS)^T per tile: the A operand comes from
-    // transpose reads of the kv tile (lane (n, g): dim 16 mb + n, keys kpi(4 g + j) and
-    // 16 + kpi(4 g + j)), the B operand from transpose reads of the tile's dS rows (source
-    // lane m of lane group g points at key kpi(4 g + m / 4), heads 16 wave + 4 (m % 4) ..).
-    f32x4 o[32];
+    // dq^T (dims x heads) += kv^T . (scale dS)^T per tile, split by latent dims: wavefront
+    // 4 + w accumulates dims [128 w, 128 w + 128) of all 64 heads, so each kv element is
+    // read from LDS once per workgroup.  The A operand comes from transpose reads of the kv
+    // tile (lane (n, g): dim 128 w + 16 mb + n, keys kpi(4 g + j) and 16 + kpi(4 g + j)),
+    // the B operands from transpose reads of the tile's dS rows (source lane m of lane
+    // group g points at key kpi(4 g + m / 4), heads 16 hb + 4 (m % 4) ..).
+    f32x4 o[32];  // o[8 hb + mb]: heads 16 hb + n, dims 128 w + 16 mb + 4 g + j
 #pragma unroll
-    for (int mb = 0; mb < 32; ++mb) o[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int offv = kpi(4 * g + (n >> 2)) * kRowStride + 8 * (n & 3);
-    const int dso = kpi(4 * g + (n >> 2)) * kDsStride + 2 * (16 * wave + 4 * (n & 3));
+    for (int k = 0; k < 32; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int offv = kpi(4 * g + (n >> 2)) * kRowStride + 8 * (n & 3) + 256 * wave;
+    const int dso = kpi(4 * g + (n >> 2)) * kDsStride + 8 * (n & 3);
     auto dq_tile = [&](int t) {
       const unsigned char* tb = kt + (t % 3) * kTileBytes;
       const unsigned char* dsr = dsb[t & 1];
-      const bf16x4 slo = ds_read_tr(dsr + dso);
-      const bf16x4 shi = ds_read_tr(dsr + dso + 16 * kDsStride);
-      const bf16x8 sf = {slo[0], slo[1], slo[2], slo[3], shi[0], shi[1], shi[2], shi[3]};
-      bf16x4 vlo[4], vhi[4];
+      bf16x8 sf[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        vlo[mb] = ds_read_tr(tb + offv + 32 * mb);
-        vhi[mb] = ds_read_tr(tb + offv + 32 * mb + 16 * kRowStride);
+      for (int hb = 0; hb < 4; ++hb) {
+        const bf16x4 slo = ds_read_tr(dsr + dso + 32 * hb);
+        const bf16x4 shi = ds_read_tr(dsr + dso + 32 * hb + 16 * kDsStride);
+        sf[hb] = bf16x8{slo[0], slo[1], slo[2], slo[3], shi[0], shi[1], shi[2], shi[3]};
       }
+      bf16x4 vlo[2], vhi[2];
+      vlo[0] = ds_read_tr(tb + offv);
+      vhi[0] = ds_read_tr(tb + offv + 16 * kRowStride);
 #pragma unroll
-      for (int mb = 0; mb < 32; ++mb) {
-        const int sl = mb % 4;
+      for (int mb = 0; mb < 8; ++mb) {
+        const int sl = mb & 1;
+        if (mb + 1 < 8) {
+          vlo[sl ^ 1] = ds_read_tr(tb + offv + 32 * (mb + 1));
+          vhi[sl ^ 1] = ds_read_tr(tb + offv + 32 * (mb + 1) + 16 * kRowStride);
+        }
         const bf16x8 av = {vlo[sl][0], vlo[sl][1], vlo[sl][2], vlo[sl][3],
                            vhi[sl][0], vhi[sl][1], vhi[sl][2], vhi[sl][3]};
-        o[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sf, o[mb], 0, 0, 0);
-        if (mb + 4 < 32) {
-          vlo[sl] = ds_read_tr(tb + offv + 32 * (mb + 4));
-          vhi[sl] = ds_read_tr(tb + offv + 32 * (mb + 4) + 16 * kRowStride);
-        }
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          o[8 * hb + mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, sf[hb], o[8 * hb + mb], 0, 0, 0);
       }
     };
     for (int t = 0; t < ntiles; ++t) {
@@ -406,26 +412,36 @@ __global__ __launch_bounds__(kPrepThreads) __attribute__((amdgpu_waves_per_eu(2,
       lds_barrier();  // the dS rows of the last tile
       dq_tile(ntiles - 1);
     }
-    // dq^T column (head 16 wave + n), dims 16 mb + 4 g + j.  The rows leave whole: this
-    // wavefront stages its 16 head rows (padded, conflict-free 8-byte writes) in a kv
-    // buffer nobody reads any more (not the last tile's; no load is in flight), then
-    // stores one 1 KiB row per instruction.  With no tile at all the q rows may still
-    // sit in buffers 1 and 2, so that case stores its (zero) rows directly.
-    auto pack = [&](int mb) {
-      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][0])) |
-                          (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][1])) << 16);
-      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[mb][2])) |
-                          (static_cast<uint32_t>(f32_to_bf16_bits(o[mb][3])) << 16);
+    // The rows leave whole: every dq wavefront writes its dims of all 64 head rows
+    // (padded, conflict-free 8-byte writes) into two kv buffers nobody reads any more (not
+    // the last tile's; no load is in flight), rows 0..31 in buffer ntiles % 3 and 32..63
+    // in the next; after a barrier each stores 16 whole rows, one 1 KiB row per
+    // instruction.  With no tile at all the q rows may still sit in buffers 1 and 2, so
+    // that case stores its (zero) rows directly.
+    auto pack = [&](int k) {
+      const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16_bits(o[k][0])) |
+                          (static_cast<uint32_t>(f32_to_bf16_bits(o[k][1])) << 16);
+      const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16_bits(o[k][2])) |
+                          (static_cast<uint32_t>(f32_to_bf16_bits(o[k][3])) << 16);
       return make_uint2(w0, w1);
     };
     if (ntiles == 0) {
-      uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * wave + n) * 512 + 4 * g;
 #pragma unroll
-      for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<uint2*>(qrow + 16 * mb) = pack(mb);
+      for (int hb = 0; hb < 4; ++hb) {
+        uint16_t* qrow = dq + (static_cast<long long>(i) * 64 + 16 * hb + n) * 512 + 128 * wave + 4 * g;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<uint2*>(qrow + 16 * mb) = pack(8 * hb + mb);
+      }
     } else {
-      unsigned char* st = kt + ((ntiles + (wave >> 1)) % 3) * kTileBytes + (16 * (wave & 1)) * kRowStride;
 #pragma unroll
-      for (int mb = 0; mb < 32; ++mb) *reinterpret_cast<uint2*>(st + n * kRowStride + 32 * mb + 8 * g) = pack(mb);
+      for (int hb = 0; hb < 4; ++hb) {
+        unsigned char* sb = kt + ((ntiles + (hb >> 1)) % 3) * kTileBytes + (16 * (hb & 1) + n) * kRowStride +
+                            256 * wave + 8 * g;
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<uint2*>(sb + 32 * mb) = pack(8 * hb + mb);
+      }
+      lds_barrier();  // every dq wavefront's dims are staged (pairs with the S wavefronts' last barrier)
+      const unsigned char* st = kt + ((ntiles + (wave >> 1)) % 3) * kTileBytes + (16 * (wave & 1)) * kRowStride;
       uint16_t* obase = dq + (static_cast<long long>(i) * 64 + 16 * wave) * 512 + 8 * lane;
 #pragma unroll
       for (int hh = 0; hh < 16; ++hh)
