@@ -171,10 +171,9 @@ __device__ __forceinline__ void write_poisoned_row(int32_t* __restrict__ out_idx
   }
 }
 
-// Candidates per LDS chunk (rows of 256 B) are a template parameter CH of the scoring
-// kernel: 128 (half the barriers) for long candidate lists, 64 (half the tail of the last
-// chunk) for short ones.  CH / 16 MFMA blocks per chunk; each of the 8 wavefronts stages
-// CH / 32 rows-of-4 (1 KiB global_load_lds) per chunk.
+// The scoring kernel's template parameters: CH candidates per LDS chunk (rows of 256 B,
+// CH / 16 MFMA blocks) and NW queries (wavefronts) per workgroup, each wavefront staging
+// CH / (4 NW) rows-of-4 (1 KiB global_load_lds) per chunk.  Launched as CH = 64, NW = 8.
 constexpr int kStages = 3;                 // chunk buffers: loads run two chunks ahead
 constexpr int kRun = 4;                    // consecutive tiles per XCD run
 
@@ -532,6 +531,7 @@ __global__ __launch_bounds__(64 * NW) void indexer_score_kernel(
     int ntile, uint32_t* __restrict__ keys) {
   __shared__ __attribute__((aligned(1024))) unsigned char kst[kStages][CH * 256];
   __shared__ int wseg[NW], wlo[NW], wnv[NW];
+  static_assert(CH % (4 * NW) == 0 && CH / (4 * NW) < 16, "chunk loads per wavefront: whole, and within vmcnt's low field");
   constexpr int NB = CH / 16;
   const int xcd = static_cast<int>(blockIdx.x) & 7, kk = static_cast<int>(blockIdx.x) >> 3;
   const int tile = ((kk / kRun) * 8 + xcd) * kRun + (kk % kRun);
