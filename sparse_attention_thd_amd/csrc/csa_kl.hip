@@ -77,8 +77,10 @@ __device__ __forceinline__ void wait_gathers(int later) {
   else __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-// Five workgroups per CU (96 registers per lane, four of them spilled; the LDS allows six):
-// 0.76 against 0.77-0.78 ms at four, 0.89 ms at six (21 registers spilled).
+// Registers held to five wavefronts per SIMD, so the top-k <= 512 instance (27 KiB of LDS,
+// six workgroups' worth per CU) runs five workgroups per CU instead of four: 96 registers
+// per lane, four of them spilled, 0.76 against 0.77-0.78 ms on the 16k pack (six, with 21
+// spilled, 0.89 ms).  The larger instance stays at two workgroups per CU (57 KiB of LDS).
 template <int NC, int KB>  // cmp_idx row chunks of kThreads entries; K stage buffers
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) void kl_query_kernel(
     const uint16_t* __restrict__ q_I, const uint16_t* __restrict__ w, const uint16_t* __restrict__ k_cmp,
