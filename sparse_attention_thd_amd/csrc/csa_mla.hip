@@ -244,7 +244,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // q rows landed everywhere -> B operand of S^T = K . Q^T.  Within MFMA step ks, k-slot
   // 8g + j of lane group g stands for latent dim 32*ks + 4*g + j (j < 4) or 32*ks + 16 +
   // 4*g + (j - 4): the same permutation the K fragments use, so each half is one
-  // conflict-free 8-byte LDS read (rows 1040 bytes apart fall 4 banks apart).
+  // conflict-free 8-byte LDS read (rows 1040 bytes apart fall 4 banks apart).  This
+  // barrier also publishes crow where a selecting query wrote its index row straight
+  // into it (no barrier of its own) before any wavefront gathers tile 0 through it.
   __builtin_amdgcn_s_waitcnt(0x0F70);
   tile_barrier();
   bf16x8 qf[16];
