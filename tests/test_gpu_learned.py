@@ -182,3 +182,36 @@ def test_learned_compressor_without_complete_groups():
     ci = compressor_inputs(7, D=64, hd=64, overlap=True, seed=14)
     bits, Tc = _run(cu_kv, ci)
     assert Tc == 0 and (bits == SENTINEL).all()
+
+
+def _random_shape(seed):
+    """Hidden size, head width, overlap, segment lengths (empty, 1-3 rows, short, long), gates."""
+    rng = np.random.default_rng(31000 + seed)
+    overlap = bool(rng.random() < 0.6)
+    D = 64 * int(rng.integers(1, 17))
+    hd = 64 * int(rng.integers(1, 9)) if overlap else 128 * int(rng.integers(1, 5))
+    nseg = int(rng.integers(1, 11))
+    kinds = rng.integers(0, 4, size=nseg)
+    lengths = [int(v) for v in np.where(kinds == 0, rng.integers(0, 4, size=nseg),
+                                        np.where(kinds == 1, rng.integers(4, 21, size=nseg),
+                                                 rng.integers(100, 1500, size=nseg)))]
+    if sum(lengths) < 4:
+        lengths.append(9)
+    peaky = rng.random() < 0.2
+    scales = dict(gate_scale=12.0, ape_scale=4.0) if peaky else {}
+    return lengths, dict(D=D, hd=hd, overlap=overlap, **scales)
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_learned_compressor_random_shapes(seed):
+    """Seeded random shapes and layouts against the oracle, with the element bound above."""
+    lengths, kw = _random_shape(seed)
+    cu_kv = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    print(f"[case] learned random{seed}: lengths={lengths} {kw}", flush=True)
+    ci = compressor_inputs(int(cu_kv[-1]), seed=100 + seed, **kw)
+    bits, Tc = _run(cu_kv, ci)
+    ref = _ref(cu_kv, ci)
+    assert Tc == ref.shape[0]
+    if Tc:
+        _close(bits[:Tc], ref, f"random{seed}")
+    assert (bits[Tc:] == SENTINEL).all()

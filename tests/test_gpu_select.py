@@ -105,3 +105,63 @@ def test_selection_is_exact_on_integer_scores(name, topk):
     assert np.all(np.isneginf(got_sc[~valid]))
     sel = int((tabs["q_cmp_nvis"] > topk).sum())
     print(f"    {sel} of {Tq} queries selected; rows and scores exact", flush=True)
+
+
+def _random_draw(seed):
+    """Layout and top-k of one seed."""
+    rng = np.random.default_rng(47000 + seed)
+    nseg = int(rng.integers(1, 5))
+    lengths = []
+    for _ in range(nseg):
+        kind = rng.random()
+        lengths.append(int(rng.integers(1, 41)) if kind < 0.3 else
+                       int(rng.integers(100, 3001)) if kind < 0.75 else int(rng.integers(4000, 9001)))
+    topk = int(rng.choice([1, 7, 64, 512, 1024, 2048]))
+    return rng, lengths, topk
+
+
+def _random_values(rng, Tc, Tq):
+    """Integer query signs, head weights and key values (scores stay exact in float32)."""
+    vmax = int(rng.choice([1, 2, 8, 64]))
+    v = rng.integers(-vmax if rng.random() < 0.5 else 0, vmax + 1, Tc)
+    if rng.random() < 0.3 and Tc > 0:
+        v[rng.integers(0, Tc, int(rng.integers(1, 6)))] = 64
+    a = rng.choice([[1], [-1, 1], [-2, -1, 1, 2], [0, 1]][int(rng.integers(0, 4))], (Tq, H_I))
+    wlo, whi = [(1, 2), (0, 3), (-2, 0), (-4, 5), (0, 1)][int(rng.integers(0, 5))]
+    w = rng.integers(wlo, whi, (Tq, H_I))
+    return a, w.astype(np.float32), v
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_selection_is_exact_on_random_layouts(seed):
+    """Seeded random layouts (1-4 segments of 1 to 9000 tokens, top-k 1 to 2048) with random
+    integer distributions: key ranges, signed or not, query signs, zero / negative / mixed
+    head weights, planted outliers; rows and scores exact as above."""
+    import sparse_attention_thd_amd as s
+    rng, lengths, topk = _random_draw(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    Tq = int(cu[-1])
+    tabs = oracle.build_indices(cu, cu, 0, Tq, R, 127, 0)
+    cu_cmp = tabs["cu_seqlens_cmp"].astype(np.int32)
+    Tc = int(cu_cmp[-1])
+    a, w, v = _random_values(rng, Tc, Tq)
+    k = np.repeat(v[:, None], D_I, axis=1).astype(np.float32)
+    print(f"[case] select random{seed}: lengths={lengths} topk={topk} Tc={Tc}", flush=True)
+    max_kv = int(np.diff(cu).max())
+    idx = torch.empty((Tq, topk), dtype=torch.int32, device="cuda")
+    sc = torch.empty((Tq, topk), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(s.csa_indexer_topk_workspace_bytes(Tq, max_kv, R), 1), dtype=torch.uint8, device="cuda")
+    dcu = torch.from_numpy(cu).cuda()
+    q_dev = _bf16(a.astype(np.float32))[:, :, None].expand(Tq, H_I, D_I).contiguous()
+    k_dev = _bf16(k) if Tc > 0 else _bf16(np.zeros((1, D_I), np.float32))
+    s.csa_indexer_topk(q_dev, _bf16(w), k_dev, Tq, Tc, H_I, D_I, dcu, dcu, torch.from_numpy(cu_cmp).cuda(), None,
+                       len(lengths), 0, R, max_kv, topk, idx, topk_score=sc, workspace=ws)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = oracle.indexer_topk(_Rows(a), w, k, tabs, topk)
+    got_idx = idx.cpu().numpy().astype(np.int64)
+    got_sc = sc.cpu().numpy().astype(np.float64)
+    bad = np.nonzero((got_idx != ref_idx).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first query {bad[0]}"
+    valid = ref_idx >= 0
+    np.testing.assert_array_equal(got_sc[valid], ref_sc[valid])
+    assert np.all(np.isneginf(got_sc[~valid]))
