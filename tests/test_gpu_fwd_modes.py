@@ -5,7 +5,8 @@
   the others without compaction; it must give bit-identical out and lse to
   CSA_IDX_ANY, which compacts every row, on the same top-k rows.
 * CSA_IDX_ANY accepts rows in any order with holes and out-of-range entries; the
-  valid entries define the set.
+  valid entries define the set (one fixed case, and seeded random layouts whose rows
+  hold random sets of distinct compressed rows, 1 to 2048 entries wide).
 * A caller-held cmp_residual equal to len mod r changes nothing; one that disagrees
   poisons exactly the queries of that segment (NaN out / lse, an all -1 top-k row),
   and csa_validate_layout names it.
@@ -16,7 +17,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_support import assert_out_close, cpu, host_view, oracle_attention, oracle_tables, run_pack, to_device
+from gpu_support import LSE_ABS, assert_out_close, cpu, host_view, oracle_attention, oracle_tables, run_pack, \
+    to_device
 from synth import make_pack, pack_from_lengths
 
 pytestmark = pytest.mark.gpu
@@ -89,6 +91,57 @@ def test_any_kind_takes_rows_in_any_order_with_holes():
     ref, _ = oracle_attention(pack, tabs, qs, cmp_kv, idx, oracle.INDEXER)
     print("   ", assert_out_close(cpu(got), ref), flush=True)
 
+
+
+def _any_rows(rng, tabs, Tq, Tc, width):
+    """Per query: a random set of distinct compressed rows (its visible range, at times
+    a few rows from anywhere in [0, Tc)), scattered over `width` entries among -1
+    holes, other negative entries and entries at or past Tc.  Returns (rows, sets):
+    the scattered rows and the same sets packed in front of -1 padding."""
+    rows = np.full((Tq, width), -1, dtype=np.int64)
+    sets = np.full((Tq, width), -1, dtype=np.int64)
+    for i in range(Tq):
+        lo, nv = int(tabs["q_cmp_lo"][i]), int(tabs["q_cmp_nvis"][i])
+        pool = list(range(lo, lo + nv))
+        if Tc > 0 and rng.random() < 0.3:
+            pool += [int(c) for c in rng.integers(0, Tc, size=int(rng.integers(1, 8)))]
+        pool = np.unique(np.asarray(pool, dtype=np.int64))
+        n = int(rng.integers(0, min(pool.size, width) + 1)) if pool.size else 0
+        chosen = rng.choice(pool, size=n, replace=False) if n else np.zeros(0, np.int64)
+        sets[i, :n] = chosen
+        junk = np.full(width - n, -1, dtype=np.int64)
+        u = rng.random(junk.size)
+        neg, past = u < 0.15, u >= 0.6
+        junk[neg] = rng.integers(-(2 ** 31), -1, size=int(neg.sum()))
+        junk[past] = np.where(rng.random(int(past.sum())) < 0.5, Tc + rng.integers(0, 1000, size=int(past.sum())),
+                              rng.integers(Tc, 2 ** 31 - 1, size=int(past.sum())))
+        rows[i] = rng.permutation(np.concatenate([chosen, junk]))
+    return rows.astype(np.int32), sets
+
+
+@pytest.mark.parametrize("seed", list(range(6)))
+def test_any_kind_random_sets_on_random_layouts(seed):
+    """Seeded random layouts (those of the random-layout tests, drawn from other seeds,
+    ratio 4): out and lse of CSA_IDX_ANY rows against oracle attention on each row's
+    set, for row widths from 1 to 2048."""
+    import sparse_attention_thd_amd as s
+    from test_gpu_random import _draw
+    p = _draw(500 + seed)
+    lengths = p.pop("lengths")
+    p["cmp_ratio"] = 4
+    pack = pack_from_lengths(f"any{seed}", lengths, seed=seed, indexer=True, **p)
+    rng = np.random.default_rng(61000 + seed)
+    width = int(rng.choice([1, 2, 16, 64, 128, 129, 200, 511, 1024, 2048]))
+    plan = run_pack(pack, return_topk_score=False)
+    tabs = oracle_tables(pack)
+    Tc = int(tabs["cu_seqlens_cmp"][-1])
+    print(f"[case] any{seed}: lengths={lengths} Tq={pack.Tq} Tc={Tc} width={width} -> CSA_IDX_ANY", flush=True)
+    rows, sets = _any_rows(rng, tabs, pack.Tq, Tc, width)
+    got, got_lse = _mla(plan, pack, torch.as_tensor(rows, device="cuda"), s.CSA_IDX_ANY)
+    cmp_kv = oracle.round_to(oracle.compress(host_view(pack, "ori_kv"), pack.cu_seqlens_kv, 4), pack.dtype)
+    ref, ref_lse = oracle_attention(pack, tabs, list(range(pack.Tq)), cmp_kv, sets, oracle.INDEXER)
+    print("   ", assert_out_close(cpu(got), ref), flush=True)
+    assert np.abs(cpu(got_lse) - ref_lse).max() <= LSE_ABS
 
 def test_residual_argument_matches_or_poisons_its_segment():
     import sparse_attention_thd_amd as s
