@@ -22,6 +22,24 @@
 namespace csa {
 namespace {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// row_to_lds for a row that one workgroup reads once (the query's q rows): the load
+// carries the non-temporal hint, so the streamed rows are the first to leave the caches
+// and the key rows that neighbouring queries share stay resident.  Measured with the
+// non-temporal output stores below: 0.998 against 1.014 ms on the 16k pack (six
+// same-box A/B pairs).  In the backward the same hints measured slower (its row
+// gradients re-read q and dout), so it keeps the plain forms.
+__device__ __forceinline__ void row_to_lds_once(const void* row_base, uint32_t lane_off, uint32_t lds_off) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 nt"
+      :
+      : "s"(lds_off), "v"(lane_off), "s"(row_base)
+      : "memory", "m0");
+}
+
 // Largest b in [0, B) with cu[b] <= x (cu non-decreasing, cu[0] <= x), found with
 // one wide load per 64 entries and a ballot instead of a chain of dependent loads.
 // The result is wave-uniform, so the loads that depend on it are scalar.
@@ -135,7 +153,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     const uint16_t* qsrc = q + (static_cast<long long>(i) * 64 + 16 * wave) * 512;
 #pragma unroll
     for (int hh = 0; hh < 16; ++hh)
-      row_to_lds(qsrc + hh * 512, lane16, kt_base + static_cast<uint32_t>((16 * wave + hh) * kRowStride));
+      row_to_lds_once(qsrc + hh * 512, lane16, kt_base + static_cast<uint32_t>((16 * wave + hh) * kRowStride));
   }
   // segment of query row i: count segment starts <= i (one ballot per 64 segments)
   int count = __popcll(__ballot(cu0 <= i));
@@ -412,12 +430,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   lds_barrier();  // every head row is complete
+  // The output rows are written once and not read again by this launch: non-temporal stores.
   uint16_t* obase = out + (static_cast<long long>(i) * 64 + 16 * wave) * 512;
 #pragma unroll
   for (int hh = 0; hh < 16; ++hh) {
     const int h = 16 * wave + hh;
-    const uint4 v = *reinterpret_cast<const uint4*>(kt + h * kRowBytes + ((el ^ swz(h)) << 4));
-    *reinterpret_cast<uint4*>(obase + hh * 512 + el * 8) = v;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(kt + h * kRowBytes + ((el ^ swz(h)) << 4));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + hh * 512 + el * 8));
   }
   if (lse != nullptr && g == 0)
     lse[static_cast<long long>(i) * 64 + head] = bad ? __builtin_nanf("") : m_run * kLn2 + logf(l_tot);
