@@ -273,7 +273,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
   // d_q rows leave as whole rows: staged in the (now idle) K stage buffers as 64 rows of
   // 256 bytes, 16-byte chunk c of row h at chunk c ^ (h & 15) (conflict-free writes),
   // then stored 1 KiB per instruction.  A wavefront's rows are its own heads, so after
-  // the barrier that frees the buffers it reads back only what it wrote itself.
+  // the barrier that frees the buffers it reads back only what it wrote itself.  The
+  // stores are non-temporal (nothing in this call reads d_q back, and the lines then
+  // leave the caches before the key rows the next queries gather): 0.734 against
+  // 0.753 ms for the whole call on the 16k pack (six same-box A/B pairs); the same hint
+  // on the q_I loads measured slower (the d_k kernel re-reads q_I).
   lds_barrier();
   unsigned char* st = &kst[0][0];
 #pragma unroll
@@ -289,8 +293,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5))) v
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = 4 * k + (lane >> 4), c = lane & 15;  // row 16 wave + r, chunk c
-    const uint4 v = *reinterpret_cast<const uint4*>(st + (16 * wave + r) * 256 + ((c ^ r) << 4));
-    *reinterpret_cast<uint4*>(obase + r * 128 + c * 8) = v;
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + (16 * wave + r) * 256 + ((c ^ r) << 4));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(obase + r * 128 + c * 8));
   }
 }
 
